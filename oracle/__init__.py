@@ -1,0 +1,40 @@
+"""CPU oracle for the tree-masked verify/expand attention path.
+
+TEST INFRASTRUCTURE ONLY.  This package is a plain, slow, float64 statement
+of what the GPU library computes.  Only the tests, the smoke check and the
+benchmark's CPU-baseline leg may import it; the library itself never does, and
+it shares no code, tables or helpers with the HIP kernels.
+
+Sources (the pages are cited by title and section/figure):
+
+* "SwiftSpec summary -- Disaggregated Speculative Decoding": draft tree
+  (Section 3.1), non-square expansion mask (Section 3.1.3, Figure 3),
+  maximum-likelihood expansion (Section 3.1.3), evolving tree cache invariant
+  and re-root (Section 3.2, Figure 4), iteration example (Section 3.1.2,
+  Figure 2).
+* "Draft-length co-design" article: acceptance up to the first mismatch plus
+  the target's own token, AL in [1, 1+D], G x (1+D) query rows per KV head
+  (its "key mechanism" and "how speculative decoding works" parts).
+
+Modules:
+
+* ``tree``      -- ancestors, depth, descendants, validity (brute force).
+* ``attention`` -- explicit-mask softmax attention in float64.
+* ``accept``    -- greedy longest accepted path by enumerating every node.
+* ``reroot``    -- evolving-tree-cache re-root and KV compaction.
+* ``topw``      -- top-w maximum-likelihood candidate selection (host side of
+  the draft expansion rounds).
+* ``bf16``      -- exact bfloat16 -> float64 decoding.
+
+Pins: every function here is checked in ``tests/test_oracle_*.py`` against
+facts fixed by the pages or by mathematics (causal attention from a library
+routine, closed forms, the Figure 2/3/4 examples, exhaustive small trees).
+The function that is not pinned by an independent fact is named in its own
+docstring ("parity unpinned").
+"""
+from .bf16 import bf16_to_f64, to_f64  # noqa: F401
+from .tree import ancestors, depth, descendants, is_valid_parent, root_path  # noqa: F401
+from .attention import tree_attention, verify, expand, gather_sequence_kv  # noqa: F401
+from .accept import accept_greedy_path, argmax_first  # noqa: F401
+from .reroot import tree_cache_reroot  # noqa: F401
+from .topw import cumulative_scores, select_top_w  # noqa: F401
