@@ -1,0 +1,191 @@
+/*
+ * tree_attn.h -- C ABI of the MI355X (gfx950) tree-masked verify/expand
+ * attention library (libtreeattn.so).
+ *
+ * The operations follow the pages this library implements:
+ *
+ *   [SS]  "SwiftSpec summary -- Disaggregated Speculative Decoding"
+ *   [DL]  "Draft-length co-design" article (speculative decoding with an AI
+ *         model co-design for faster LLM inference)
+ *   [MD]  "MineDraft notes" (batch parallelism)
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Tree.  A draft tree holds one token per node; parent -> child means "the
+ *   child's token follows the parent's" ([SS] Section 3.1).  Nodes are stored
+ *   in topological order: -1 <= parent[b*n_max + i] < i.  parent = -1 marks a
+ *   child of the root, and the root is the last token of the prefix cache.
+ *   On the target side the root token itself is node 0 (parent[0] = -1,
+ *   parent[i] >= 0 for i >= 1), so verifying 1 + D tokens means n = 1 + D
+ *   query nodes ([DL] key mechanism).  At most TA_MAX_NODES nodes.
+ *
+ * KV cache.  One layer's keys and values ([SS] Section 3.2 invariant):
+ *   positions 0 .. P-1 of a sequence hold the prefix cache (verified tokens),
+ *   position P + i holds tree node i.  P = prefix_len[b] and the tree size
+ *   n = n_nodes[b] live in device memory, so a whole step can be captured in
+ *   a HIP graph without host synchronisation.
+ *   - contiguous:  K, V are [B][T_cap][Hkv][d]
+ *   - paged:       K, V are [num_blocks][block_size][Hkv][d]; position t of
+ *                  sequence b is block block_table[b*max_blocks + t/block_size],
+ *                  slot t % block_size ([MD] Section 5.3, vLLM KV blocks).
+ *   Elements are fp32 or bf16 (TA_F32 / TA_BF16); d is 64 or 128.
+ *
+ * Grouped-query attention.  G = Hq / Hkv query heads share one KV head; query
+ *   head h reads KV head h / G ([DL] key mechanism: G = query heads per KV
+ *   head, G x (1 + D) query rows per KV head).
+ *
+ * Memory and errors.  Every array argument is a device pointer unless the
+ *   comment says "host".  The caller allocates and owns everything, including
+ *   the attention workspace; the library allocates nothing and keeps no state
+ *   between calls.  Calls are asynchronous on `stream` (a hipStream_t; NULL
+ *   is the default stream) and return a ta_status synchronously for problems
+ *   the host can see (null pointers, unsupported sizes or dtypes, workspace
+ *   too small, a failed launch).  Device-side preconditions (valid parent
+ *   arrays, P + n <= T_cap, valid block ids, a root path in `path`, finite
+ *   logits) are the caller's; when they are violated the results are
+ *   unspecified, but the kernels clamp every index so that no access leaves
+ *   the buffers described here.
+ */
+#ifndef TREE_ATTN_H
+#define TREE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TA_MAX_NODES 256   /* tree capacity per sequence (4 x 64-bit masks) */
+
+typedef enum {
+  TA_OK = 0,
+  TA_ERR_INVALID_ARG = -1,     /* null pointer, negative size, Hq % Hkv != 0, ... */
+  TA_ERR_UNSUPPORTED = -2,     /* d not in {64,128}, unknown dtype, ...          */
+  TA_ERR_TREE_TOO_LARGE = -3,  /* n_max > TA_MAX_NODES                           */
+  TA_ERR_WORKSPACE = -4,       /* workspace missing or smaller than required     */
+  TA_ERR_HIP = -5              /* a HIP runtime call or kernel launch failed     */
+} ta_status;
+
+typedef enum { TA_F32 = 0, TA_BF16 = 1 } ta_dtype;
+
+/* One layer's KV cache.  block_table == NULL selects the contiguous layout. */
+typedef struct {
+  void* k;                       /* keys   (layout above)                          */
+  void* v;                       /* values (same layout as k)                      */
+  const int32_t* block_table;    /* paged: [B][max_blocks] physical block ids      */
+  int32_t block_size;            /* paged: tokens per block (> 0)                  */
+  int32_t max_blocks;            /* paged: columns of block_table                  */
+  int32_t num_blocks;            /* paged: blocks in the pool (ids are < this)     */
+  int32_t T_cap;                 /* contiguous: tokens per sequence in k and v;
+                                    paged: logical capacity, <= max_blocks*block_size */
+} ta_kv;
+
+/* Optional tuning/testing knobs for the attention calls (NULL = automatic). */
+typedef struct {
+  int32_t chunk_tokens;  /* KV tokens per split-KV work item, a multiple of 64; 0 = auto */
+  int32_t kernel;        /* 0 = auto, 1 = generic fp32-math kernel, 2 = bf16 MFMA kernel */
+} ta_attn_opts;
+
+/*
+ * Workspace (bytes) needed by tree_attn_verify / tree_attn_expand for these
+ * sizes.  n_q is n_max for verify and w for expand.  The workspace holds
+ * split-KV partial results and one arrival counter per work group; it must
+ * be zero-filled before its first use, and every call leaves the counters at
+ * zero again, so one zeroed buffer can be reused for any later call of the
+ * same or smaller size on the same stream (overlapping calls that share a
+ * workspace race).  Returns 0 when no split is needed, or (size_t)-1 for
+ * invalid sizes.
+ */
+size_t tree_attn_workspace_bytes(int B, int n_q, int Hq, int Hkv, int d, int dtype, int T_cap,
+                                 const ta_attn_opts* opts);
+
+/*
+ * Tree-masked verification attention ([SS] Section 3.1.2 Figure 2 target
+ * side; [DL] key mechanism: the 1 + D drafted tokens are checked in one
+ * pass).  Query rows are every tree node i < n_nodes[b]; row i attends to all
+ * P prefix positions and to the tree positions of its ancestors and itself.
+ *
+ *   q      [B][n_max][Hq][d]  (dtype)  queries, already position-rotated
+ *   out    [B][n_max][Hq][d]  (dtype)  softmax(scale*q.k^T restricted) . v,
+ *                                      rounded to nearest-even for bf16
+ *   lse    [B][Hq][n_max]     fp32     natural-log log-sum-exp of the scaled,
+ *                                      masked scores (may be NULL)
+ *   Rows i >= n_nodes[b] of out and lse are not written.
+ *   The queries' own K/V must already sit at positions P + i.
+ */
+int tree_attn_verify(const void* q, ta_kv kv, const int32_t* prefix_len, const int32_t* parent,
+                     const int32_t* n_nodes, int B, int n_max, int Hq, int Hkv, int d, int dtype,
+                     float scale, void* out, float* lse, void* ws, size_t ws_bytes,
+                     const ta_attn_opts* opts, void* stream);
+
+/*
+ * Tree-masked expansion attention ([SS] Section 3.1.3 Figure 3: w new
+ * leaves x (prefix + tree) non-square mask).  Query row r is tree node
+ * n_nodes[b] - w + r (the w newest nodes, whose K/V are already appended);
+ * rows with a negative node index are not written.
+ *
+ *   q, out [B][w][Hq][d] (dtype);  lse [B][Hq][w] fp32 (may be NULL)
+ */
+int tree_attn_expand(const void* q, ta_kv kv, const int32_t* prefix_len, const int32_t* parent,
+                     const int32_t* n_nodes, int B, int w, int n_max, int Hq, int Hkv, int d,
+                     int dtype, float scale, void* out, float* lse, void* ws, size_t ws_bytes,
+                     const ta_attn_opts* opts, void* stream);
+
+/*
+ * Greedy longest accepted path ([DL] how speculative decoding works and the
+ * Acceptance Length entry: accept up to the first mismatch, then the
+ * target's own token; AL in [1, 1 + D]).
+ *
+ *   logits   [B][n_max][V]  fp32 or bf16 (logit_dtype); row i is the target's
+ *                           distribution after node i
+ *   tok      [B][n_max]     int32 draft token of each node
+ *   root_tok [B]            int32 the target's token after the last prefix
+ *                           token (on the target side: the root token, tok[0])
+ *   path     [B][n_max]     int32 out: node ids of the accepted path from the
+ *                           top of the tree, then -1
+ *   path_len [B]            int32 out: its length (= AL on the target side)
+ *   bonus    [B]            int32 out: the target's next token after the path
+ *
+ * a[i] = argmax of row i (lowest index on ties).  Node i is accepted when
+ * every node u on its root path has tok[u] == (parent[u] < 0 ? root_tok :
+ * a[parent[u]]).  The deepest accepted node wins (lowest index on ties);
+ * bonus = a[best], or root_tok when nothing is accepted.
+ */
+int accept_greedy_path(const void* logits, int logit_dtype, const int32_t* parent,
+                       const int32_t* tok, const int32_t* n_nodes, const int32_t* root_tok, int B,
+                       int n_max, int V, int32_t* path, int32_t* path_len, int32_t* bonus,
+                       void* stream);
+
+/*
+ * Evolving-tree-cache re-root with in-place KV compaction ([SS] Section 3.2,
+ * Figure 4; Section 3.1.2 Figure 2).  For each sequence with k = path_len[b]
+ * and path v_0 .. v_{k-1} (a root path of the tree):
+ *   - rows P + v_j move to P + j (the verified nodes join the prefix);
+ *   - if keep_subtree[b] and k > 0, the descendants of v_{k-1}, in their
+ *     original order, move to P + k, P + k + 1, ...; their parents are
+ *     renumbered and children of v_{k-1} get parent -1;
+ *   - prefix_len[b] += k; n_nodes[b] = number of kept nodes; parent entries
+ *     past it are set to -1.  k == 0 with keep is a no-op; k == 0 without
+ *     keep drops the tree.
+ * Every layer in kv_layers (a HOST array of n_layers descriptors, K and V,
+ * all with the same dtype, Hkv and d) is compacted bit for bit; rows at or
+ * past the new end are left unspecified.  prefix_len, parent and n_nodes are
+ * updated in place after all layers have been moved.
+ */
+int tree_cache_reroot(const ta_kv* kv_layers, int n_layers, int32_t* prefix_len, int32_t* parent,
+                      int32_t* n_nodes, const int32_t* path, const int32_t* path_len,
+                      const uint8_t* keep_subtree, int B, int n_max, int Hkv, int d, int dtype,
+                      void* stream);
+
+/* Human-readable name of a ta_status value (static string). */
+const char* ta_status_string(int status);
+
+/* Library version, e.g. "0.1.0" (static string). */
+const char* ta_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TREE_ATTN_H */

@@ -1,0 +1,99 @@
+"""Shared test helpers: upload seeded cases to the GPU, compare against the
+oracle with the stated tolerances."""
+import os
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# Float parity bars (against the float64 oracle):
+#   fp32: |x - ref| <= 1e-5 * |ref| + 1e-5 * max|ref| over the (sequence, head) block
+#   bf16: |x - ref| <= 1e-2 * |ref| + 2e-2
+FP32_RTOL = 1e-5
+BF16_ATOL, BF16_RTOL = 2e-2, 1e-2
+
+
+def ensure_built():
+    import tree_masked_verify_attn_amd as ta
+    from tree_masked_verify_attn_amd import build as b
+    if not os.path.exists(b.LIB):
+        b.build()
+    return ta.load_library()
+
+
+def dev_tensor(arr, dtype_name=None, device="cuda"):
+    """numpy -> device tensor; uint16 arrays with dtype 'bf16' become bfloat16."""
+    import torch
+    if dtype_name == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(arr)).to(device)
+
+
+def to_f64(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        bits = t.view(torch.int16).cpu().numpy().view(np.uint16)
+        return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return t.cpu().numpy().astype(np.float64)
+
+
+class DevCase:
+    """Device copies of a gen.Case's arrays plus a KVCache."""
+
+    def __init__(self, case, device="cuda"):
+        import tree_masked_verify_attn_amd as ta
+        self.case = case
+        dt = case.dtype
+        self.q = dev_tensor(case.q, dt, device)
+        self.k = dev_tensor(case.k, dt, device)
+        self.v = dev_tensor(case.v, dt, device)
+        self.prefix_len = dev_tensor(case.prefix_len.astype(np.int32), device=device)
+        self.parent = dev_tensor(case.parent.astype(np.int32), device=device)
+        self.n_nodes = dev_tensor(case.n_nodes.astype(np.int32), device=device)
+        self.block_table = (dev_tensor(case.block_table.astype(np.int32), device=device)
+                            if case.block_table is not None else None)
+        self.kv = ta.KVCache(self.k, self.v, self.block_table,
+                             T_cap=case.T_cap if case.block_table is not None else None)
+        if case.tok is not None:
+            self.tok = dev_tensor(case.tok.astype(np.int32), device=device)
+            self.root_tok = dev_tensor(case.root_tok.astype(np.int32), device=device)
+        if case.logits is not None:
+            self.logits = dev_tensor(case.logits, device=device)
+
+
+def assert_attn_close(O, L, O_ref, L_ref, dtype, rows_mask=None, what=""):
+    """Elementwise bars; rows_mask [B][n_q] selects rows that are outputs."""
+    O_ref = np.asarray(O_ref)
+    L_ref = np.asarray(L_ref)
+    B, n_q, Hq, d = O_ref.shape
+    if rows_mask is None:
+        rows_mask = ~np.isnan(O_ref[:, :, 0, 0])
+    worst = 0.0
+    for b in range(B):
+        rows = np.nonzero(rows_mask[b])[0]
+        if rows.size == 0:
+            continue
+        for h in range(Hq):
+            o, r = O[b, rows, h], O_ref[b, rows, h]
+            l, lr = L[b, h, rows], L_ref[b, h, rows]
+            if dtype == "f32":
+                atol_o = FP32_RTOL * np.abs(r).max()
+                atol_l = FP32_RTOL * np.abs(lr).max()
+                bound_o = atol_o + FP32_RTOL * np.abs(r)
+                bound_l = atol_l + FP32_RTOL * np.abs(lr)
+            else:
+                bound_o = BF16_ATOL + BF16_RTOL * np.abs(r)
+                bound_l = BF16_ATOL + BF16_RTOL * np.abs(lr)
+            eo = np.abs(o - r)
+            el = np.abs(l - lr)
+            if not (np.all(eo <= bound_o) and np.all(el <= bound_l)):
+                i = np.unravel_index(np.argmax(eo - bound_o), eo.shape)
+                raise AssertionError(
+                    f"{what} b={b} h={h}: max|dO|={eo.max():.3e} (bound at worst "
+                    f"{bound_o[i]:.3e}), max|dLSE|={el.max():.3e}, any NaN="
+                    f"{np.isnan(o).any() or np.isnan(l).any()}")
+            worst = max(worst, float((eo / bound_o).max()), float((el / bound_l).max()))
+    return worst

@@ -1,0 +1,113 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects
+host-checkable bad arguments before touching a device (no compute here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from helpers import ROOT, ensure_built
+
+import tree_masked_verify_attn_amd as ta
+from tree_masked_verify_attn_amd import _lib
+
+
+def test_header_declares_exactly_the_bound_symbols():
+    hdr = open(os.path.join(ROOT, "include", "tree_attn.h")).read()
+    declared = set(re.findall(r"^\s*(?:size_t|int|const char\*)\s+(\w+)\(", hdr, re.M))
+    assert declared == set(_lib.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_symbol():
+    lib = ensure_built()
+    for name in _lib.EXPORTED_SYMBOLS:
+        assert hasattr(lib, name), name
+    out = os.popen(f"nm -D --defined-only {_lib.LIB_PATH}").read()
+    for name in _lib.EXPORTED_SYMBOLS:
+        assert re.search(rf"\bT {name}$", out, re.M), name
+    assert ta.ta_version() == "0.1.0"
+    for st in (0, -1, -2, -3, -4, -5):
+        assert ta.ta_status_string(st).startswith("TA_")
+
+
+def _kv(T_cap=64, paged=False):
+    if paged:
+        return _lib.ta_kv(0x1000, 0x2000, 0x3000, 16, 4, 8, T_cap)
+    return _lib.ta_kv(0x1000, 0x2000, None, 0, 0, 0, T_cap)
+
+
+def _verify(lib, **kw):
+    a = dict(q=0x4000, kv=_kv(), P=0x5000, par=0x6000, n=0x7000, B=2, n_max=16, Hq=8, Hkv=2,
+             d=128, dt=ta.TA_BF16, scale=0.1, out=0x8000, lse=0x9000, ws=0xa000, wsb=1 << 30)
+    a.update(kw)
+    return lib.tree_attn_verify(a["q"], a["kv"], a["P"], a["par"], a["n"], a["B"], a["n_max"],
+                                a["Hq"], a["Hkv"], a["d"], a["dt"], ctypes.c_float(a["scale"]),
+                                a["out"], a["lse"], a["ws"], a["wsb"], None, None)
+
+
+def test_invalid_arguments_are_rejected_on_the_host():
+    lib = ensure_built()
+    assert _verify(lib, Hq=7) == _lib.TA_ERR_INVALID_ARG          # Hq % Hkv != 0
+    assert _verify(lib, d=96) == _lib.TA_ERR_UNSUPPORTED
+    assert _verify(lib, dt=7) == _lib.TA_ERR_UNSUPPORTED
+    assert _verify(lib, n_max=257) == _lib.TA_ERR_TREE_TOO_LARGE
+    assert _verify(lib, q=None) == _lib.TA_ERR_INVALID_ARG
+    assert _verify(lib, scale=0.0) == _lib.TA_ERR_INVALID_ARG
+    assert _verify(lib, kv=_lib.ta_kv(0x1000, None, None, 0, 0, 0, 64)) == _lib.TA_ERR_INVALID_ARG
+    # paged capacity larger than the block table can address
+    assert _verify(lib, kv=_lib.ta_kv(0x1000, 0x2000, 0x3000, 16, 4, 8, 65)) == \
+        _lib.TA_ERR_INVALID_ARG
+    assert _verify(lib, B=0) == _lib.TA_OK                        # nothing to do
+    # a plan that splits needs a workspace
+    need = ta.tree_attn_workspace_bytes(1, 16, 8, 2, 128, ta.TA_BF16, 64, chunk_tokens=64)
+    assert need == 0
+    need = ta.tree_attn_workspace_bytes(2, 16, 8, 2, 128, ta.TA_BF16, 4096, chunk_tokens=256)
+    assert need > 0
+    opts = _lib.ta_attn_opts(256, 0)
+    st = lib.tree_attn_verify(0x4000, _kv(4096), 0x5000, 0x6000, 0x7000, 2, 16, 8, 2, 128,
+                              ta.TA_BF16, ctypes.c_float(0.1), 0x8000, None, None, 0,
+                              ctypes.byref(opts), None)
+    assert st == _lib.TA_ERR_WORKSPACE
+    st = lib.tree_attn_verify(0x4000, _kv(4096), 0x5000, 0x6000, 0x7000, 2, 16, 8, 2, 128,
+                              ta.TA_BF16, ctypes.c_float(0.1), 0x8000, None, 0xa000, need - 1,
+                              ctypes.byref(opts), None)
+    assert st == _lib.TA_ERR_WORKSPACE
+    bad = _lib.ta_attn_opts(100, 0)                               # not a multiple of 64
+    st = lib.tree_attn_verify(0x4000, _kv(4096), 0x5000, 0x6000, 0x7000, 2, 16, 8, 2, 128,
+                              ta.TA_BF16, ctypes.c_float(0.1), 0x8000, None, 0xa000, 1 << 30,
+                              ctypes.byref(bad), None)
+    assert st == _lib.TA_ERR_UNSUPPORTED
+    # expand: w must lie in [1, n_max]
+    st = lib.tree_attn_expand(0x4000, _kv(), 0x5000, 0x6000, 0x7000, 2, 17, 16, 8, 2, 128,
+                              ta.TA_BF16, ctypes.c_float(0.1), 0x8000, None, 0xa000, 1 << 30,
+                              None, None)
+    assert st == _lib.TA_ERR_INVALID_ARG
+    # accept
+    st = lib.accept_greedy_path(0x1000, ta.TA_F32, 0x2000, 0x3000, 0x4000, 0x5000, 2, 300, 10,
+                                0x6000, 0x7000, 0x8000, None)
+    assert st == _lib.TA_ERR_TREE_TOO_LARGE
+    st = lib.accept_greedy_path(0x1000, 5, 0x2000, 0x3000, 0x4000, 0x5000, 2, 16, 10, 0x6000,
+                                0x7000, 0x8000, None)
+    assert st == _lib.TA_ERR_UNSUPPORTED
+    st = lib.accept_greedy_path(None, ta.TA_F32, 0x2000, 0x3000, 0x4000, 0x5000, 2, 16, 10,
+                                0x6000, 0x7000, 0x8000, None)
+    assert st == _lib.TA_ERR_INVALID_ARG
+    # re-root
+    arr = (_lib.ta_kv * 1)(_kv())
+    st = lib.tree_cache_reroot(arr, 1, 0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, 2, 16, 2,
+                               80, ta.TA_BF16, None)
+    assert st == _lib.TA_ERR_UNSUPPORTED
+    st = lib.tree_cache_reroot(arr, 1, None, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, 2, 16, 2,
+                               128, ta.TA_BF16, None)
+    assert st == _lib.TA_ERR_INVALID_ARG
+    arr2 = (_lib.ta_kv * 1)(_lib.ta_kv(0x1001, 0x2000, None, 0, 0, 0, 64))   # misaligned
+    st = lib.tree_cache_reroot(arr2, 1, 0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, 2, 16, 2,
+                               128, ta.TA_BF16, None)
+    assert st == _lib.TA_ERR_INVALID_ARG
+
+
+def test_workspace_query_rejects_bad_sizes():
+    ensure_built()
+    with pytest.raises(ta.TreeAttnError):
+        ta.tree_attn_workspace_bytes(1, 4, 6, 4, 128, ta.TA_BF16, 100)
+    assert ta.tree_attn_workspace_bytes(0, 4, 8, 4, 128, ta.TA_BF16, 100) == 0

@@ -1,0 +1,136 @@
+"""GPU parity of tree_attn_verify / tree_attn_expand against the float64 oracle
+(small seeded cases spanning several KV tiles, splits and a ragged tail)."""
+import numpy as np
+import pytest
+
+from helpers import DevCase, assert_attn_close, ensure_built, to_f64
+
+import oracle
+from gen import config1_tiny, random_case
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ta():
+    ensure_built()
+    import tree_masked_verify_attn_amd as m
+    return m
+
+
+def _run_verify(ta, dc, chunk=0, kernel=0):
+    import torch
+    c = dc.case
+    out = torch.full_like(dc.q, float("nan"))
+    lse = torch.full((c.B, c.Hq, c.n_max), float("nan"), dtype=torch.float32, device=dc.q.device)
+    ta.tree_attn_verify(dc.q, dc.kv, dc.prefix_len, dc.parent, dc.n_nodes, c.scale, out=out,
+                        lse=lse, chunk_tokens=chunk, kernel=kernel)
+    torch.cuda.synchronize()
+    return to_f64(out), lse.cpu().numpy().astype(np.float64)
+
+
+def _check_unwritten(O, L, c, q_nodes_of):
+    for b in range(c.B):
+        n = int(c.n_nodes[b])
+        for r, node in enumerate(q_nodes_of(n)):
+            if not (0 <= node < n):
+                assert np.isnan(O[b, r]).all() and np.isnan(L[b, :, r]).all(), (b, r)
+
+
+@pytest.mark.parametrize("chunk", [0, 64, 128])
+def test_tiny_fp32_verify_and_expand(ta, chunk):
+    import torch
+    c = config1_tiny()
+    dc = DevCase(c)
+    O, L = _run_verify(ta, dc, chunk)
+    Or, Lr = oracle.verify(c)
+    assert_attn_close(O, L, Or, Lr, "f32", what="verify")
+    w = c.planted["expand_w"]
+    qe = dc.q[:, c.n_max - w:].contiguous()
+    out, lse = ta.tree_attn_expand(qe, dc.kv, dc.prefix_len, dc.parent, dc.n_nodes, c.scale,
+                                   chunk_tokens=chunk)
+    torch.cuda.synchronize()
+    Oer, Ler = oracle.expand(c, c.q[:, c.n_max - w:], w)
+    assert Oer.shape[1] == 4 and c.prefix_len[0] + c.n_nodes[0] == 144   # the 4 x 144 mask
+    assert_attn_close(to_f64(out), lse.cpu().numpy(), Oer, Ler, "f32", what="expand")
+
+
+CASES = [
+    # (seed, B, Hq, Hkv, d, P_range, n_max, dtype, target_side, paged, chunk)
+    (1, 3, 8, 1, 64, (0, 300), 16, "f32", False, False, 64),
+    (2, 4, 8, 2, 128, (0, 300), 16, "bf16", False, False, 0),
+    (3, 4, 16, 2, 128, (100, 700), 8, "bf16", True, False, 128),
+    (4, 2, 4, 4, 64, (0, 200), 12, "bf16", False, True, 64),
+    (5, 5, 6, 3, 128, (1, 520), 20, "f32", True, True, 192),
+    (6, 2, 64, 8, 128, (60, 400), 16, "bf16", True, False, 64),
+    (7, 3, 32, 8, 128, (0, 257), 40, "bf16", False, False, 0),
+    (8, 2, 2, 1, 128, (0, 5), 256, "bf16", False, False, 64),   # maximum tree size
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"seed{c[0]}" for c in CASES])
+def test_random_verify(ta, case):
+    seed, B, Hq, Hkv, d, P_range, n_max, dtype, target_side, paged, chunk = case
+    c = random_case(seed, B, Hq, Hkv, d, P_range=P_range, n_max=n_max, dtype=dtype,
+                    target_side=target_side, paged=paged)
+    print(f"case seed={seed} B={B} Hq={Hq} Hkv={Hkv} d={d} n_max={n_max} {dtype} paged={paged}",
+          flush=True)
+    dc = DevCase(c)
+    O, L = _run_verify(ta, dc, chunk)
+    Or, Lr = oracle.verify(c)
+    assert_attn_close(O, L, Or, Lr, dtype, what=f"seed{seed}")
+    _check_unwritten(O, L, c, lambda n: range(c.n_max))
+
+
+@pytest.mark.parametrize("w", [1, 3, 8])
+def test_random_expand(ta, w):
+    import torch
+    c = random_case(40 + w, 3, 8, 2, 128, P_range=(0, 200), n_max=12, n_range=(1, 12),
+                    dtype="bf16")
+    dc = DevCase(c)
+    qe_np = c.q[:, :w]
+    qe = dc.q[:, :w].contiguous()
+    out = torch.full_like(qe, float("nan"))
+    lse = torch.full((c.B, c.Hq, w), float("nan"), dtype=torch.float32, device=qe.device)
+    ta.tree_attn_expand(qe, dc.kv, dc.prefix_len, dc.parent, dc.n_nodes, c.scale, out=out,
+                        lse=lse, chunk_tokens=64)
+    torch.cuda.synchronize()
+    O, L = to_f64(out), lse.cpu().numpy()
+    Or, Lr = oracle.expand(c, qe_np, w)
+    assert_attn_close(O, L, Or, Lr, "bf16", what=f"expand w={w}")
+    _check_unwritten(O, L, c, lambda n: [n - w + r for r in range(w)])
+
+
+def test_split_count_invariance(ta):
+    c = random_case(77, 2, 16, 2, 128, P_range=(900, 1100), n_max=8, dtype="bf16",
+                    target_side=True)
+    dc = DevCase(c)
+    ref = None
+    for chunk in (64, 256, 1024, 2048):
+        O, L = _run_verify(ta, dc, chunk)
+        if ref is None:
+            ref = (O, L)
+            Or, Lr = oracle.verify(c)
+            assert_attn_close(O, L, Or, Lr, "bf16", what=f"chunk {chunk}")
+        else:
+            assert np.abs(O - ref[0]).max() < 4e-3 and np.abs(L - ref[1]).max() < 1e-4
+
+
+def test_repeated_calls_are_deterministic_and_reset_counters(ta):
+    c = random_case(78, 3, 8, 2, 128, P_range=(300, 900), n_max=16, dtype="bf16")
+    dc = DevCase(c)
+    O1, L1 = _run_verify(ta, dc, 64)
+    for _ in range(3):
+        O2, L2 = _run_verify(ta, dc, 64)
+        np.testing.assert_array_equal(O1, O2)
+        np.testing.assert_array_equal(L1, L2)
+
+
+def test_zero_prefix_and_empty_trees(ta):
+    c = random_case(79, 4, 8, 2, 64, P_range=(0, 0), n_max=6, n_range=(0, 6), dtype="f32")
+    c.n_nodes[1] = 0
+    dc = DevCase(c)
+    O, L = _run_verify(ta, dc, 0)
+    Or, Lr = oracle.verify(c)
+    assert_attn_close(O, L, Or, Lr, "f32", what="P=0")
+    assert np.isnan(O[1]).all()

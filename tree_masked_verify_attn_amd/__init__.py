@@ -1,0 +1,30 @@
+"""MI355X (gfx950) tree-masked verify/expand attention for speculative decoding.
+
+The compute lives in ``libtreeattn.so`` (hand-written HIP kernels behind the C
+ABI of ``include/tree_attn.h``); this package is its ctypes binding.  The
+entry points keep the C names:
+
+* ``tree_attn_verify``   -- tree-masked attention over every draft node
+* ``tree_attn_expand``   -- the same for the w newest leaves (non-square mask)
+* ``accept_greedy_path`` -- greedy longest accepted path, AL and bonus token
+* ``tree_cache_reroot``  -- evolving-tree-cache re-root with in-place KV moves
+"""
+from ._lib import (  # noqa: F401
+    EXPORTED_SYMBOLS,
+    KVCache,
+    TA_BF16,
+    TA_F32,
+    TA_MAX_NODES,
+    TreeAttnError,
+    Workspace,
+    accept_greedy_path,
+    load_library,
+    ta_status_string,
+    ta_version,
+    tree_attn_expand,
+    tree_attn_verify,
+    tree_attn_workspace_bytes,
+    tree_cache_reroot,
+)
+
+__version__ = "0.1.0"

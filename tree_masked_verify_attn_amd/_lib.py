@@ -1,0 +1,366 @@
+"""ctypes binding of libtreeattn.so (the C ABI declared in include/tree_attn.h).
+
+Argument marshalling only: tensors are checked for shape, dtype, device and
+contiguity, their device pointers and torch's current HIP stream are passed
+to the library, and status codes become exceptions.  Every step of the hot
+path runs in the library's HIP kernels; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import List, Optional, Sequence
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libtreeattn.so")
+
+TA_OK = 0
+TA_ERR_INVALID_ARG = -1
+TA_ERR_UNSUPPORTED = -2
+TA_ERR_TREE_TOO_LARGE = -3
+TA_ERR_WORKSPACE = -4
+TA_ERR_HIP = -5
+TA_F32 = 0
+TA_BF16 = 1
+TA_MAX_NODES = 256
+
+#: Every symbol include/tree_attn.h declares.
+EXPORTED_SYMBOLS = (
+    "tree_attn_workspace_bytes",
+    "tree_attn_verify",
+    "tree_attn_expand",
+    "accept_greedy_path",
+    "tree_cache_reroot",
+    "ta_status_string",
+    "ta_version",
+)
+
+
+class TreeAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+class ta_kv(ctypes.Structure):
+    _fields_ = [
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p),
+        ("block_size", ctypes.c_int32),
+        ("max_blocks", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("T_cap", ctypes.c_int32),
+    ]
+
+
+class ta_attn_opts(ctypes.Structure):
+    _fields_ = [("chunk_tokens", ctypes.c_int32), ("kernel", ctypes.c_int32)]
+
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libtreeattn.so (raises if it has not been built)."""
+    global _lib
+    with _lib_lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is missing: build the HIP library first "
+                "(python -m tree_masked_verify_attn_amd.build)")
+        lib = ctypes.CDLL(path)
+        c_int, c_size, vp, f32 = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+        lib.tree_attn_workspace_bytes.argtypes = [c_int] * 7 + [ctypes.POINTER(ta_attn_opts)]
+        lib.tree_attn_workspace_bytes.restype = c_size
+        attn = [vp, ta_kv, vp, vp, vp]
+        lib.tree_attn_verify.argtypes = attn + [c_int] * 6 + [f32, vp, vp, vp, c_size,
+                                                              ctypes.POINTER(ta_attn_opts), vp]
+        lib.tree_attn_verify.restype = c_int
+        lib.tree_attn_expand.argtypes = attn + [c_int] * 7 + [f32, vp, vp, vp, c_size,
+                                                              ctypes.POINTER(ta_attn_opts), vp]
+        lib.tree_attn_expand.restype = c_int
+        lib.accept_greedy_path.argtypes = [vp, c_int, vp, vp, vp, vp, c_int, c_int, c_int, vp, vp,
+                                           vp, vp]
+        lib.accept_greedy_path.restype = c_int
+        lib.tree_cache_reroot.argtypes = [ctypes.POINTER(ta_kv), c_int, vp, vp, vp, vp, vp, vp,
+                                          c_int, c_int, c_int, c_int, c_int, vp]
+        lib.tree_cache_reroot.restype = c_int
+        lib.ta_status_string.argtypes = [c_int]
+        lib.ta_status_string.restype = ctypes.c_char_p
+        lib.ta_version.argtypes = []
+        lib.ta_version.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+def _check(status: int):
+    if status != TA_OK:
+        msg = load_library().ta_status_string(status).decode()
+        raise TreeAttnError(status, msg)
+
+
+def ta_status_string(status: int) -> str:
+    return load_library().ta_status_string(status).decode()
+
+
+def ta_version() -> str:
+    return load_library().ta_version().decode()
+
+
+# ----------------------------------------------------------------------------
+# tensor marshalling
+# ----------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return TA_F32
+    if t.dtype == torch.bfloat16:
+        return TA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; expected float32 or bfloat16")
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def _need(t, name, dtype=None, ndim=None, device=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    return t
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+class KVCache:
+    """One layer's K/V cache.
+
+    Contiguous: ``k``, ``v`` are ``[B][T_cap][Hkv][d]``.  Paged: ``k``, ``v``
+    are ``[num_blocks][block_size][Hkv][d]`` and ``block_table`` is
+    ``[B][max_blocks]`` int32; ``T_cap`` defaults to ``max_blocks * block_size``.
+    """
+
+    def __init__(self, k, v, block_table=None, T_cap: Optional[int] = None):
+        torch = _torch()
+        _need(k, "k", ndim=4)
+        _need(v, "v", dtype=k.dtype, ndim=4, device=k.device)
+        if tuple(k.shape) != tuple(v.shape):
+            raise ValueError("k and v must have the same shape")
+        self.k, self.v = k, v
+        self.block_table = block_table
+        if block_table is not None:
+            _need(block_table, "block_table", dtype=torch.int32, ndim=2, device=k.device)
+            self.block_size = int(k.shape[1])
+            self.max_blocks = int(block_table.shape[1])
+            self.num_blocks = int(k.shape[0])
+            self.T_cap = int(T_cap) if T_cap is not None else self.max_blocks * self.block_size
+        else:
+            self.block_size = self.max_blocks = self.num_blocks = 0
+            self.T_cap = int(k.shape[1]) if T_cap is None else int(T_cap)
+        self.Hkv = int(k.shape[2])
+        self.d = int(k.shape[3])
+
+    @property
+    def dtype(self):
+        return self.k.dtype
+
+    def struct(self) -> ta_kv:
+        return ta_kv(self.k.data_ptr(), self.v.data_ptr(), _ptr(self.block_table),
+                     self.block_size, self.max_blocks, self.num_blocks, self.T_cap)
+
+
+def _opts(chunk_tokens: int = 0, kernel: int = 0):
+    if not chunk_tokens and not kernel:
+        return None
+    return ctypes.byref(ta_attn_opts(int(chunk_tokens), int(kernel)))
+
+
+def tree_attn_workspace_bytes(B: int, n_q: int, Hq: int, Hkv: int, d: int, dtype: int,
+                              T_cap: int, chunk_tokens: int = 0, kernel: int = 0) -> int:
+    n = load_library().tree_attn_workspace_bytes(B, n_q, Hq, Hkv, d, dtype, T_cap,
+                                                 _opts(chunk_tokens, kernel))
+    if n == ctypes.c_size_t(-1).value:
+        raise TreeAttnError(TA_ERR_INVALID_ARG, "invalid sizes for a workspace query")
+    return int(n)
+
+
+class Workspace:
+    """A zero-initialised device buffer reused across attention calls.
+
+    The library leaves its arrival counters at zero after every call, so the
+    buffer only grows (and is re-zeroed) when a larger plan needs more room.
+    Calls sharing one workspace must be ordered (one stream).
+    """
+
+    def __init__(self, device=None):
+        self.device = device
+        self.buf = None
+
+    def get(self, nbytes: int):
+        torch = _torch()
+        if nbytes == 0:
+            return None
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.zeros(nbytes + 256, dtype=torch.uint8, device=self.device)
+        return self.buf
+
+
+_default_ws = {}
+
+
+def _workspace_for(device, nbytes):
+    key = str(device)
+    ws = _default_ws.get(key)
+    if ws is None:
+        ws = _default_ws[key] = Workspace(device)
+    return ws.get(nbytes)
+
+
+def _attention(fn_name, q, kv: KVCache, prefix_len, parent, n_nodes, scale, out, lse, workspace,
+               w, chunk_tokens, kernel, stream, with_lse):
+    torch = _torch()
+    lib = load_library()
+    _need(q, "q", dtype=kv.dtype, ndim=4, device=kv.k.device)
+    dev = kv.k.device
+    _need(prefix_len, "prefix_len", dtype=torch.int32, ndim=1, device=dev)
+    _need(parent, "parent", dtype=torch.int32, ndim=2, device=dev)
+    _need(n_nodes, "n_nodes", dtype=torch.int32, ndim=1, device=dev)
+    B, n_q, Hq, d = (int(x) for x in q.shape)
+    n_max = int(parent.shape[1])
+    if parent.shape[0] != B or prefix_len.shape[0] != B or n_nodes.shape[0] != B:
+        raise ValueError("batch size mismatch between q and prefix_len/parent/n_nodes")
+    if d != kv.d:
+        raise ValueError("head dim of q and kv differ")
+    if kv.block_table is not None and kv.block_table.shape[0] != B:
+        raise ValueError("block_table must have one row per sequence")
+    if kv.block_table is None and kv.k.shape[0] != B:
+        raise ValueError("contiguous k/v must have one row per sequence")
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", dtype=q.dtype, device=dev)
+        if tuple(out.shape) != tuple(q.shape):
+            raise ValueError("out must have q's shape")
+    if lse is None and with_lse:
+        lse = torch.empty((B, Hq, n_q), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", dtype=torch.float32, device=dev)
+        if tuple(lse.shape) != (B, Hq, n_q):
+            raise ValueError("lse must be [B][Hq][n_q]")
+    nbytes = tree_attn_workspace_bytes(B, n_q, Hq, kv.Hkv, d, dt, kv.T_cap, chunk_tokens, kernel)
+    if workspace is None:
+        ws = _workspace_for(dev, nbytes)
+    else:
+        ws = workspace.get(nbytes) if isinstance(workspace, Workspace) else workspace
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    common = (q.data_ptr(), kv.struct(), prefix_len.data_ptr(), parent.data_ptr(),
+              n_nodes.data_ptr())
+    tail = (ctypes.c_float(scale), out.data_ptr(), _ptr(lse), _ptr(ws), ws_bytes,
+            _opts(chunk_tokens, kernel), _stream(stream))
+    if fn_name == "verify":
+        if n_q != n_max:
+            raise ValueError("verify queries must be [B][n_max][Hq][d]")
+        st = lib.tree_attn_verify(*common, B, n_max, Hq, kv.Hkv, d, dt, *tail)
+    else:
+        st = lib.tree_attn_expand(*common, B, w, n_max, Hq, kv.Hkv, d, dt, *tail)
+    _check(st)
+    return out, lse
+
+
+def tree_attn_verify(q, kv: KVCache, prefix_len, parent, n_nodes, scale: float, out=None,
+                     lse=None, workspace=None, chunk_tokens: int = 0, kernel: int = 0,
+                     stream=None, with_lse: bool = True):
+    """Verification attention over every tree node; returns ``(out, lse)``."""
+    return _attention("verify", q, kv, prefix_len, parent, n_nodes, scale, out, lse, workspace,
+                      0, chunk_tokens, kernel, stream, with_lse)
+
+
+def tree_attn_expand(q, kv: KVCache, prefix_len, parent, n_nodes, scale: float, out=None,
+                     lse=None, workspace=None, chunk_tokens: int = 0, kernel: int = 0,
+                     stream=None, with_lse: bool = True):
+    """Expansion attention for the ``w = q.shape[1]`` newest nodes; returns ``(out, lse)``."""
+    return _attention("expand", q, kv, prefix_len, parent, n_nodes, scale, out, lse, workspace,
+                      int(q.shape[1]), chunk_tokens, kernel, stream, with_lse)
+
+
+def accept_greedy_path(logits, parent, tok, n_nodes, root_tok, path=None, path_len=None,
+                       bonus=None, stream=None):
+    """Greedy longest accepted path; returns ``(path, path_len, bonus)`` int32 tensors."""
+    torch = _torch()
+    lib = load_library()
+    _need(logits, "logits", ndim=3)
+    dev = logits.device
+    _need(parent, "parent", dtype=torch.int32, ndim=2, device=dev)
+    _need(tok, "tok", dtype=torch.int32, ndim=2, device=dev)
+    _need(n_nodes, "n_nodes", dtype=torch.int32, ndim=1, device=dev)
+    _need(root_tok, "root_tok", dtype=torch.int32, ndim=1, device=dev)
+    B, n_max, V = (int(x) for x in logits.shape)
+    if tuple(parent.shape) != (B, n_max) or tuple(tok.shape) != (B, n_max):
+        raise ValueError("parent/tok must be [B][n_max] matching logits")
+    if path is None:
+        path = torch.empty((B, n_max), dtype=torch.int32, device=dev)
+    if path_len is None:
+        path_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    if bonus is None:
+        bonus = torch.empty((B,), dtype=torch.int32, device=dev)
+    st = lib.accept_greedy_path(logits.data_ptr(), _dtype_code(logits), parent.data_ptr(),
+                                tok.data_ptr(), n_nodes.data_ptr(), root_tok.data_ptr(), B, n_max,
+                                V, path.data_ptr(), path_len.data_ptr(), bonus.data_ptr(),
+                                _stream(stream))
+    _check(st)
+    return path, path_len, bonus
+
+
+def tree_cache_reroot(kv_layers: Sequence[KVCache], prefix_len, parent, n_nodes, path, path_len,
+                      keep_subtree, stream=None):
+    """In-place re-root of every layer's cache and of prefix_len/parent/n_nodes."""
+    torch = _torch()
+    lib = load_library()
+    dev = parent.device
+    _need(prefix_len, "prefix_len", dtype=torch.int32, ndim=1, device=dev)
+    _need(parent, "parent", dtype=torch.int32, ndim=2, device=dev)
+    _need(n_nodes, "n_nodes", dtype=torch.int32, ndim=1, device=dev)
+    _need(path, "path", dtype=torch.int32, ndim=2, device=dev)
+    _need(path_len, "path_len", dtype=torch.int32, ndim=1, device=dev)
+    _need(keep_subtree, "keep_subtree", dtype=torch.uint8, ndim=1, device=dev)
+    B, n_max = (int(x) for x in parent.shape)
+    layers: List[KVCache] = list(kv_layers)
+    if layers:
+        Hkv, d, dtype = layers[0].Hkv, layers[0].d, layers[0].dtype
+        for L in layers:
+            if (L.Hkv, L.d, L.dtype) != (Hkv, d, dtype) or L.k.device != dev:
+                raise ValueError("all layers must share Hkv, d, dtype and device")
+        dt = _dtype_code(layers[0].k)
+    else:
+        Hkv, d, dt = 1, 128, TA_BF16
+    arr = (ta_kv * max(1, len(layers)))(*[L.struct() for L in layers])
+    st = lib.tree_cache_reroot(arr, len(layers), prefix_len.data_ptr(), parent.data_ptr(),
+                               n_nodes.data_ptr(), path.data_ptr(), path_len.data_ptr(),
+                               keep_subtree.data_ptr(), B, n_max, Hkv, d, dt, _stream(stream))
+    _check(st)

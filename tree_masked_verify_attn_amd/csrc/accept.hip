@@ -1,0 +1,200 @@
+// Greedy longest accepted path (draft-length co-design article: accept draft
+// tokens up to the first mismatch with the target's greedy choice, then the
+// target's own token; SwiftSpec summary, Section 3.1.2 Figure 2: the target
+// returns the root, the accepted nodes and one new token).
+//
+// Two launches:
+//   1. argmax: one work group per (node, sequence) scans the node's logits row
+//      with 16-byte loads and a wave64 (value, index) max-reduction; ties go
+//      to the lowest index.  The result a[i] is parked in path[b][i].
+//   2. path: one work group per sequence, one thread per node.  Ancestor
+//      bitmasks come from pointer doubling; "token matches the target's
+//      choice after the parent" is a wave ballot into a 256-bit mask; a node
+//      is accepted when its ancestor mask has no bit outside that mask; the
+//      deepest accepted node (popcount of its mask, lowest index on ties)
+//      wins and its mask, read in index order, is the path.
+#include "ta_device.h"
+
+namespace ta {
+namespace {
+
+constexpr int kThreads = 256;
+
+struct ArgMax {
+  float v;
+  int i;
+};
+
+__device__ __forceinline__ ArgMax better(ArgMax a, ArgMax b) {
+  if (b.v > a.v || (b.v == a.v && b.i < a.i)) return b;
+  return a;
+}
+
+__device__ __forceinline__ void consider(ArgMax& best, float v, int i) {
+  if (v > best.v) {  // indices grow within a thread: strict '>' keeps the first
+    best.v = v;
+    best.i = i;
+  }
+}
+
+template <bool kBf16>
+__global__ __launch_bounds__(kThreads) void argmax_kernel(const void* logits, const int32_t* n_nodes,
+                                                          int n_max, int V, int32_t* path) {
+  const int i = blockIdx.x;
+  const int b = blockIdx.y;
+  int n = n_nodes[b];
+  n = n < 0 ? 0 : (n > n_max ? n_max : n);
+  if (i >= n) return;
+  const int tid = threadIdx.x;
+  ArgMax best{-INFINITY, 0x7fffffff};
+  const size_t row = (static_cast<size_t>(b) * n_max + i) * static_cast<size_t>(V);
+  if (kBf16) {
+    const uint16_t* x = static_cast<const uint16_t*>(logits) + row;
+    const bool vec = (V % 8 == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
+    int start = 0;
+    if (vec) {
+      const u32x4* x4 = reinterpret_cast<const u32x4*>(x);
+      const int nv = V / 8;
+      for (int j = tid; j < nv; j += kThreads) {
+        const u32x4 w = __builtin_nontemporal_load(x4 + j);
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          consider(best, __uint_as_float(ws[e] << 16), 8 * j + 2 * e);
+          consider(best, __uint_as_float(ws[e] & 0xffff0000u), 8 * j + 2 * e + 1);
+        }
+      }
+      start = V;
+    }
+    for (int j = start + tid; j < V; j += kThreads) consider(best, bf16_bits_to_f32(x[j]), j);
+  } else {
+    const float* x = static_cast<const float*>(logits) + row;
+    const bool vec = (V % 4 == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
+    int start = 0;
+    if (vec) {
+      const f32x4* x4 = reinterpret_cast<const f32x4*>(x);
+      const int nv = V / 4;
+      for (int j = tid; j < nv; j += kThreads) {
+        const f32x4 w = __builtin_nontemporal_load(x4 + j);
+        consider(best, w.x, 4 * j);
+        consider(best, w.y, 4 * j + 1);
+        consider(best, w.z, 4 * j + 2);
+        consider(best, w.w, 4 * j + 3);
+      }
+      start = V;
+    }
+    for (int j = start + tid; j < V; j += kThreads) consider(best, x[j], j);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    ArgMax other{__shfl_xor(best.v, o, 64), __shfl_xor(best.i, o, 64)};
+    best = better(best, other);
+  }
+  __shared__ ArgMax sBest[kThreads / 64];
+  if ((tid & 63) == 0) sBest[tid >> 6] = best;
+  __syncthreads();
+  if (tid == 0) {
+    ArgMax r = sBest[0];
+    for (int w = 1; w < kThreads / 64; ++w) r = better(r, sBest[w]);
+    // Every row has at least one element; an all-NaN row reports index 0.
+    path[static_cast<size_t>(b) * n_max + i] = (r.i == 0x7fffffff) ? 0 : r.i;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void accept_path_kernel(const int32_t* parent,
+                                                               const int32_t* tok,
+                                                               const int32_t* n_nodes,
+                                                               const int32_t* root_tok, int n_max,
+                                                               int32_t* path, int32_t* path_len,
+                                                               int32_t* bonus) {
+  __shared__ uint64_t sAnc[kMaxNodes][kMaskWords];
+  __shared__ int sJump[kMaxNodes];
+  __shared__ int sA[kMaxNodes];
+  __shared__ uint64_t sAcc[kMaskWords];
+  __shared__ unsigned long long sKey[kThreads / 64];
+  const int b = blockIdx.x;
+  const int i = threadIdx.x;
+  int n = n_nodes[b];
+  n = n < 0 ? 0 : (n > n_max ? n_max : n);
+  const int32_t* par_b = parent + static_cast<size_t>(b) * n_max;
+  int32_t* path_b = path + static_cast<size_t>(b) * n_max;
+  const int rt = root_tok[b];
+
+  if (i < n) sA[i] = path_b[i];  // argmax parked by the first launch
+  if (i < kMaskWords) sAcc[i] = 0;
+  build_ancestor_masks(par_b, n, sAnc, sJump);  // synchronises (also after the reads above)
+
+  bool acc = false;
+  if (i < n) {
+    const int p = clamp_parent(par_b[i], i);
+    acc = tok[static_cast<size_t>(b) * n_max + i] == (p < 0 ? rt : sA[p]);
+  }
+  const unsigned long long bal = __ballot(acc);  // 64 nodes per wave -> mask word (i >> 6)
+  if ((i & 63) == 0) sAcc[i >> 6] = bal;
+  __syncthreads();
+
+  unsigned long long key = 0;  // (depth << 16) | (0xffff - node); 0 = not accepted
+  if (i < n) {
+    bool ok = true;
+    int depth = 0;
+#pragma unroll
+    for (int w = 0; w < kMaskWords; ++w) {
+      ok = ok && ((sAnc[i][w] & ~sAcc[w]) == 0);
+      depth += __popcll(sAnc[i][w]);
+    }
+    if (ok) key = (static_cast<unsigned long long>(depth) << 16) | (0xffffu - i);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned long long other = __shfl_xor(key, o, 64);
+    key = other > key ? other : key;
+  }
+  if ((i & 63) == 0) sKey[i >> 6] = key;
+  __syncthreads();
+  unsigned long long best_key = sKey[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) best_key = sKey[w] > best_key ? sKey[w] : best_key;
+
+  const int best = best_key ? static_cast<int>(0xffffu - (best_key & 0xffffu)) : -1;
+  const int len = best_key ? static_cast<int>(best_key >> 16) : 0;
+  // Write the path: node j of best's mask goes to slot popcount(mask below j).
+  if (i < n_max) {
+    int slot = -1;
+    if (best >= 0 && i < n && mask_bit(sAnc[best], i)) {
+      slot = 0;
+      for (int w = 0; w < kMaskWords; ++w) {
+        const uint64_t m = sAnc[best][w];
+        if (w < (i >> 6))
+          slot += __popcll(m);
+        else if (w == (i >> 6))
+          slot += __popcll(m & ((1ull << (i & 63)) - 1ull));
+      }
+    }
+    if (slot >= 0) path_b[slot] = i;
+    if (i >= len) path_b[i] = -1;
+  }
+  if (i == 0) {
+    path_len[b] = len;
+    bonus[b] = best >= 0 ? sA[best] : rt;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_accept(const void* logits, int logit_dtype, const int32_t* parent,
+                         const int32_t* tok, const int32_t* n_nodes, const int32_t* root_tok,
+                         int B, int n_max, int V, int32_t* path, int32_t* path_len,
+                         int32_t* bonus, hipStream_t s) {
+  dim3 g1(n_max, B);
+  if (logit_dtype == TA_BF16)
+    argmax_kernel<true><<<g1, kThreads, 0, s>>>(logits, n_nodes, n_max, V, path);
+  else
+    argmax_kernel<false><<<g1, kThreads, 0, s>>>(logits, n_nodes, n_max, V, path);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  accept_path_kernel<<<B, kThreads, 0, s>>>(parent, tok, n_nodes, root_tok, n_max, path, path_len,
+                                            bonus);
+  return hipGetLastError();
+}
+
+}  // namespace ta

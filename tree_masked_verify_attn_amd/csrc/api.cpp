@@ -1,0 +1,257 @@
+// C ABI of libtreeattn: host-side validation, split planning and launches.
+// Declarations and semantics: include/tree_attn.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "ta_internal.h"
+#include "tree_attn.h"
+
+namespace {
+
+using ta::AttnParams;
+
+int device_cu_count() {
+  // Compute units of the current device (cached per device id).
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  if (dev < 64) cache[dev] = cus;
+  return cus;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int kGenericRows = 32;
+constexpr int kMfmaRows = 128;  // query rows (G x nodes) per MFMA work group, at most
+
+struct Plan {
+  int kernel;         // 1 generic, 2 mfma
+  int rows_per_tile;
+  int n_row_tiles;
+  int chunk;
+  int n_split;
+  size_t ws_bytes;
+};
+
+int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+// Chooses the kernel, the row tiling and the split-KV chunk.  The automatic
+// chunk gives about two work groups per compute unit, never below 256 KV
+// positions per split (smaller chunks cost more in partial results than they
+// gain in parallelism).
+bool make_plan(int B, int n_q, int Hq, int Hkv, int d, int dtype, int T_cap,
+               const ta_attn_opts* opts, Plan& pl) {
+  const int G = Hq / Hkv;
+  const int R = n_q * G;
+  int kernel = opts ? opts->kernel : 0;
+  const bool mfma_ok = dtype == TA_BF16 && (d == 128 || d == 64) && false;
+  if (kernel == 0) kernel = mfma_ok ? 2 : 1;
+  if (kernel == 2 && !mfma_ok) return false;
+  if (kernel != 1 && kernel != 2) return false;
+  pl.kernel = kernel;
+  pl.rows_per_tile = kernel == 2 ? kMfmaRows : kGenericRows;
+  pl.n_row_tiles = (R + pl.rows_per_tile - 1) / pl.rows_per_tile;
+  const long long items = static_cast<long long>(B) * Hkv * pl.n_row_tiles;
+  int chunk = opts ? opts->chunk_tokens : 0;
+  if (chunk < 0 || chunk % 64 != 0) return false;
+  if (chunk == 0) {
+    const long long want = 2LL * device_cu_count();
+    long long splits = items > 0 ? (want + items - 1) / items : 1;
+    splits = std::max(1LL, splits);
+    chunk = round_up(static_cast<int>((T_cap + splits - 1) / splits), 64);
+    chunk = std::max(chunk, 256);
+  }
+  chunk = std::max(64, std::min(chunk, round_up(std::max(T_cap, 1), 64)));
+  pl.chunk = chunk;
+  pl.n_split = (T_cap + chunk - 1) / chunk;
+  if (pl.n_split < 1) pl.n_split = 1;
+  const int tiles = B * Hkv * pl.n_row_tiles;
+  pl.ws_bytes = ta::attn_ws_bytes(tiles, pl.n_split, pl.rows_per_tile, d);
+  return true;
+}
+
+int check_common(int B, int n_q, int n_max, int Hq, int Hkv, int d, int dtype, int T_cap) {
+  if (B < 0 || n_q < 1 || n_max < 1 || Hq < 1 || Hkv < 1 || T_cap < 1) return TA_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return TA_ERR_INVALID_ARG;
+  if (dtype != TA_F32 && dtype != TA_BF16) return TA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return TA_ERR_UNSUPPORTED;
+  if (n_max > TA_MAX_NODES) return TA_ERR_TREE_TOO_LARGE;
+  return TA_OK;
+}
+
+int check_kv(const ta_kv& kv) {
+  if (kv.k == nullptr || kv.v == nullptr || kv.T_cap < 1) return TA_ERR_INVALID_ARG;
+  if (kv.block_table != nullptr) {
+    if (kv.block_size < 1 || kv.max_blocks < 1 || kv.num_blocks < 1) return TA_ERR_INVALID_ARG;
+    if (static_cast<long long>(kv.max_blocks) * kv.block_size < kv.T_cap)
+      return TA_ERR_INVALID_ARG;
+  }
+  return TA_OK;
+}
+
+int run_attention(const void* q, ta_kv kv, const int32_t* prefix_len, const int32_t* parent,
+                  const int32_t* n_nodes, int B, int n_q, int n_max, int expand, int Hq, int Hkv,
+                  int d, int dtype, float scale, void* out, float* lse, void* ws,
+                  size_t ws_bytes, const ta_attn_opts* opts, void* stream) {
+  int st = check_common(B, n_q, n_max, Hq, Hkv, d, dtype, kv.T_cap);
+  if (st != TA_OK) return st;
+  st = check_kv(kv);
+  if (st != TA_OK) return st;
+  if (q == nullptr || out == nullptr || prefix_len == nullptr || parent == nullptr ||
+      n_nodes == nullptr)
+    return TA_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || scale != scale) return TA_ERR_INVALID_ARG;
+  if (B == 0) return TA_OK;
+  Plan pl;
+  if (!make_plan(B, n_q, Hq, Hkv, d, dtype, kv.T_cap, opts, pl)) return TA_ERR_UNSUPPORTED;
+  if (pl.kernel == 2 && !(aligned16(q) && aligned16(out) && aligned16(kv.k) && aligned16(kv.v)))
+    return TA_ERR_INVALID_ARG;
+  if (pl.ws_bytes > 0 && (ws == nullptr || ws_bytes < pl.ws_bytes || !aligned16(ws)))
+    return TA_ERR_WORKSPACE;
+
+  AttnParams p{};
+  p.q = q;
+  p.out = out;
+  p.lse = lse;
+  p.k = kv.k;
+  p.v = kv.v;
+  p.block_table = kv.block_table;
+  p.block_size = kv.block_size;
+  p.max_blocks = kv.max_blocks;
+  p.num_blocks = kv.num_blocks;
+  p.T_cap = kv.T_cap;
+  p.prefix_len = prefix_len;
+  p.parent = parent;
+  p.n_nodes = n_nodes;
+  p.B = B;
+  p.n_max = n_max;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.d = d;
+  p.G = Hq / Hkv;
+  p.n_q = n_q;
+  p.expand = expand;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.chunk = pl.chunk;
+  p.n_split = pl.n_split;
+  p.rows_per_tile = pl.rows_per_tile;
+  p.n_row_tiles = pl.n_row_tiles;
+  if (pl.ws_bytes > 0) {
+    const int tiles = B * Hkv * pl.n_row_tiles;
+    const size_t parts = static_cast<size_t>(tiles) * pl.n_split * pl.rows_per_tile;
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    p.ws_o = reinterpret_cast<float*>(base);
+    p.ws_ml = reinterpret_cast<float*>(base + parts * d * sizeof(float));
+    size_t off = parts * d * sizeof(float) + parts * 2 * sizeof(float);
+    off = (off + 255) & ~static_cast<size_t>(255);
+    p.ws_cnt = reinterpret_cast<int32_t*>(base + off);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = pl.kernel == 2 ? ta::launch_attn_mfma(p, s) : ta::launch_attn_generic(p, dtype, s);
+  return e == hipSuccess ? TA_OK : TA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t tree_attn_workspace_bytes(int B, int n_q, int Hq, int Hkv, int d, int dtype, int T_cap,
+                                 const ta_attn_opts* opts) {
+  if (check_common(B, n_q, n_q, Hq, Hkv, d, dtype, T_cap) != TA_OK) return static_cast<size_t>(-1);
+  if (B == 0) return 0;
+  Plan pl;
+  if (!make_plan(B, n_q, Hq, Hkv, d, dtype, T_cap, opts, pl)) return static_cast<size_t>(-1);
+  return pl.ws_bytes;
+}
+
+int tree_attn_verify(const void* q, ta_kv kv, const int32_t* prefix_len, const int32_t* parent,
+                     const int32_t* n_nodes, int B, int n_max, int Hq, int Hkv, int d, int dtype,
+                     float scale, void* out, float* lse, void* ws, size_t ws_bytes,
+                     const ta_attn_opts* opts, void* stream) {
+  return run_attention(q, kv, prefix_len, parent, n_nodes, B, n_max, n_max, 0, Hq, Hkv, d, dtype,
+                       scale, out, lse, ws, ws_bytes, opts, stream);
+}
+
+int tree_attn_expand(const void* q, ta_kv kv, const int32_t* prefix_len, const int32_t* parent,
+                     const int32_t* n_nodes, int B, int w, int n_max, int Hq, int Hkv, int d,
+                     int dtype, float scale, void* out, float* lse, void* ws, size_t ws_bytes,
+                     const ta_attn_opts* opts, void* stream) {
+  if (w < 1 || w > n_max) return TA_ERR_INVALID_ARG;
+  return run_attention(q, kv, prefix_len, parent, n_nodes, B, w, n_max, 1, Hq, Hkv, d, dtype,
+                       scale, out, lse, ws, ws_bytes, opts, stream);
+}
+
+int accept_greedy_path(const void* logits, int logit_dtype, const int32_t* parent,
+                       const int32_t* tok, const int32_t* n_nodes, const int32_t* root_tok, int B,
+                       int n_max, int V, int32_t* path, int32_t* path_len, int32_t* bonus,
+                       void* stream) {
+  if (B < 0 || n_max < 1 || V < 1) return TA_ERR_INVALID_ARG;
+  if (n_max > TA_MAX_NODES) return TA_ERR_TREE_TOO_LARGE;
+  if (logit_dtype != TA_F32 && logit_dtype != TA_BF16) return TA_ERR_UNSUPPORTED;
+  if (logits == nullptr || parent == nullptr || tok == nullptr || n_nodes == nullptr ||
+      root_tok == nullptr || path == nullptr || path_len == nullptr || bonus == nullptr)
+    return TA_ERR_INVALID_ARG;
+  if (B == 0) return TA_OK;
+  hipError_t e = ta::launch_accept(logits, logit_dtype, parent, tok, n_nodes, root_tok, B, n_max,
+                                   V, path, path_len, bonus, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TA_OK : TA_ERR_HIP;
+}
+
+int tree_cache_reroot(const ta_kv* kv_layers, int n_layers, int32_t* prefix_len, int32_t* parent,
+                      int32_t* n_nodes, const int32_t* path, const int32_t* path_len,
+                      const uint8_t* keep_subtree, int B, int n_max, int Hkv, int d, int dtype,
+                      void* stream) {
+  if (B < 0 || n_layers < 0 || n_max < 1 || Hkv < 1) return TA_ERR_INVALID_ARG;
+  if (n_max > TA_MAX_NODES) return TA_ERR_TREE_TOO_LARGE;
+  if (dtype != TA_F32 && dtype != TA_BF16) return TA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return TA_ERR_UNSUPPORTED;
+  if (prefix_len == nullptr || parent == nullptr || n_nodes == nullptr || path == nullptr ||
+      path_len == nullptr || keep_subtree == nullptr || (n_layers > 0 && kv_layers == nullptr))
+    return TA_ERR_INVALID_ARG;
+  for (int i = 0; i < n_layers; ++i) {
+    const int st = check_kv(kv_layers[i]);
+    if (st != TA_OK) return st;
+    if (!aligned16(kv_layers[i].k) || !aligned16(kv_layers[i].v)) return TA_ERR_INVALID_ARG;
+  }
+  if (B == 0) return TA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int row_bytes = d * (dtype == TA_BF16 ? 2 : 4);
+  for (int l0 = 0; l0 < n_layers; l0 += ta::kRerootMaxLayersPerLaunch) {
+    const int cnt = std::min(ta::kRerootMaxLayersPerLaunch, n_layers - l0);
+    ta::RerootLayers L{};
+    for (int i = 0; i < cnt; ++i) {
+      const ta_kv& kv = kv_layers[l0 + i];
+      L.l[i] = ta::RerootLayer{kv.k, kv.v, kv.block_table, kv.block_size, kv.max_blocks,
+                               kv.num_blocks, kv.T_cap};
+    }
+    hipError_t e = ta::launch_reroot_move(L, cnt, prefix_len, parent, n_nodes, path, path_len,
+                                          keep_subtree, B, n_max, Hkv, row_bytes, s);
+    if (e != hipSuccess) return TA_ERR_HIP;
+  }
+  hipError_t e = ta::launch_reroot_meta(prefix_len, parent, n_nodes, path, path_len, keep_subtree,
+                                        B, n_max, s);
+  return e == hipSuccess ? TA_OK : TA_ERR_HIP;
+}
+
+const char* ta_status_string(int status) {
+  switch (status) {
+    case TA_OK: return "TA_OK";
+    case TA_ERR_INVALID_ARG: return "TA_ERR_INVALID_ARG: invalid argument";
+    case TA_ERR_UNSUPPORTED: return "TA_ERR_UNSUPPORTED: unsupported size or dtype";
+    case TA_ERR_TREE_TOO_LARGE: return "TA_ERR_TREE_TOO_LARGE: more than 256 tree nodes";
+    case TA_ERR_WORKSPACE: return "TA_ERR_WORKSPACE: workspace missing or too small";
+    case TA_ERR_HIP: return "TA_ERR_HIP: HIP launch or runtime failure";
+    default: return "unknown ta_status";
+  }
+}
+
+const char* ta_version(void) { return "0.1.0"; }
+
+}  // extern "C"

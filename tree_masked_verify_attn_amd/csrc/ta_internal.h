@@ -1,0 +1,73 @@
+// Internal declarations shared by the HIP translation units of libtreeattn.
+// Public API: include/tree_attn.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tree_attn.h"
+
+namespace ta {
+
+// ---------------------------------------------------------------------------
+// Plain-old-data parameter block of one attention launch (passed by value).
+// ---------------------------------------------------------------------------
+struct AttnParams {
+  const void* q;
+  void* out;
+  float* lse;
+  const void* k;
+  const void* v;
+  const int32_t* block_table;  // nullptr: contiguous layout
+  int32_t block_size, max_blocks, num_blocks, T_cap;
+  const int32_t* prefix_len;
+  const int32_t* parent;
+  const int32_t* n_nodes;
+  int32_t B, n_max, Hq, Hkv, d, G;
+  int32_t n_q;          // query rows per sequence in q/out (n_max or w)
+  int32_t expand;       // 0: row r is node r; 1: row r is node n - n_q + r
+  float scale_log2;     // softmax scale * log2(e): scores are kept in log2 units
+  // split-KV plan
+  int32_t chunk;        // KV tokens per split (multiple of 64)
+  int32_t n_split;      // splits allocated per (b, kv head, row tile)
+  int32_t rows_per_tile;
+  int32_t n_row_tiles;
+  // workspace (only when n_split > 1)
+  float* ws_o;          // [tiles][n_split][rows_per_tile][d] unnormalised partial outputs
+  float* ws_ml;         // [tiles][n_split][rows_per_tile][2]  running max (log2) and sum
+  int32_t* ws_cnt;      // [tiles] arrival counters (zero between calls)
+};
+
+// Workspace layout for a plan; returns bytes.
+size_t attn_ws_bytes(int tiles, int n_split, int rows_per_tile, int d);
+
+hipError_t launch_attn_generic(const AttnParams& p, int dtype, hipStream_t s);
+hipError_t launch_attn_mfma(const AttnParams& p, hipStream_t s);
+
+// Accept: argmax pass (writes a[i] into path) then the path pass.
+hipError_t launch_accept(const void* logits, int logit_dtype, const int32_t* parent,
+                         const int32_t* tok, const int32_t* n_nodes, const int32_t* root_tok,
+                         int B, int n_max, int V, int32_t* path, int32_t* path_len,
+                         int32_t* bonus, hipStream_t s);
+
+// Re-root: one launch per group of layers moves rows, then one updates metadata.
+constexpr int kRerootMaxLayersPerLaunch = 32;
+struct RerootLayer {
+  void* k;
+  void* v;
+  const int32_t* block_table;
+  int32_t block_size, max_blocks, num_blocks, T_cap;
+};
+struct RerootLayers {
+  RerootLayer l[kRerootMaxLayersPerLaunch];
+};
+hipError_t launch_reroot_move(const RerootLayers& layers, int n_layers,
+                              const int32_t* prefix_len, const int32_t* parent,
+                              const int32_t* n_nodes, const int32_t* path,
+                              const int32_t* path_len, const uint8_t* keep, int B, int n_max,
+                              int Hkv, int row_bytes, hipStream_t s);
+hipError_t launch_reroot_meta(int32_t* prefix_len, int32_t* parent, int32_t* n_nodes,
+                              const int32_t* path, const int32_t* path_len, const uint8_t* keep,
+                              int B, int n_max, hipStream_t s);
+
+}  // namespace ta
