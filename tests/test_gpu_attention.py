@@ -134,3 +134,20 @@ def test_zero_prefix_and_empty_trees(ta):
     Or, Lr = oracle.verify(c)
     assert_attn_close(O, L, Or, Lr, "f32", what="P=0")
     assert np.isnan(O[1]).all()
+
+
+def test_workspace_reuse_across_plans(ta):
+    """One workspace serves calls with different plans (split counts, tiles)."""
+    ws = ta.Workspace()
+    cases = [random_case(80 + i, 2 + i, 8, 2, 128, P_range=(300, 900 + 300 * i), n_max=8 + 4 * i,
+                         dtype="bf16") for i in range(3)]
+    for rep in range(2):
+        for i, c in enumerate(cases):
+            dc = DevCase(c)
+            import torch
+            out, lse = ta.tree_attn_verify(dc.q, dc.kv, dc.prefix_len, dc.parent, dc.n_nodes,
+                                           c.scale, workspace=ws, chunk_tokens=64 * (i + 1))
+            torch.cuda.synchronize()
+            Or, Lr = oracle.verify(c)
+            assert_attn_close(to_f64(out), lse.cpu().numpy(), Or, Lr, "bf16",
+                              what=f"rep {rep} case {i}")

@@ -212,9 +212,10 @@ def tree_attn_workspace_bytes(B: int, n_q: int, Hq: int, Hkv: int, d: int, dtype
 class Workspace:
     """A zero-initialised device buffer reused across attention calls.
 
-    The library leaves its arrival counters at zero after every call, so the
-    buffer only grows (and is re-zeroed) when a larger plan needs more room.
-    Calls sharing one workspace must be ordered (one stream).
+    The library keeps its arrival counters in a fixed slab at the start of the
+    buffer and leaves them at zero after every call, so the buffer is zeroed
+    only when it is (re)allocated, and any later call may reuse it.  Calls
+    sharing one workspace must be ordered (one stream).
     """
 
     def __init__(self, device=None):

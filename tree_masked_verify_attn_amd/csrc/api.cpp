@@ -72,8 +72,14 @@ bool make_plan(int B, int n_q, int Hq, int Hkv, int d, int dtype, int T_cap,
   pl.chunk = chunk;
   pl.n_split = (T_cap + chunk - 1) / chunk;
   if (pl.n_split < 1) pl.n_split = 1;
-  const int tiles = B * Hkv * pl.n_row_tiles;
-  pl.ws_bytes = ta::attn_ws_bytes(tiles, pl.n_split, pl.rows_per_tile, d);
+  const long long tiles = static_cast<long long>(B) * Hkv * pl.n_row_tiles;
+  if (pl.n_split > 1 && tiles > ta::kMaxTiles) {
+    // more work groups than counters: fall back to one split when possible
+    if (opts && opts->chunk_tokens) return false;
+    pl.chunk = round_up(std::max(T_cap, 1), 64);
+    pl.n_split = 1;
+  }
+  pl.ws_bytes = ta::attn_ws_bytes(static_cast<int>(tiles), pl.n_split, pl.rows_per_tile, d);
   return true;
 }
 
@@ -147,11 +153,9 @@ int run_attention(const void* q, ta_kv kv, const int32_t* prefix_len, const int3
     const int tiles = B * Hkv * pl.n_row_tiles;
     const size_t parts = static_cast<size_t>(tiles) * pl.n_split * pl.rows_per_tile;
     uint8_t* base = static_cast<uint8_t*>(ws);
-    p.ws_o = reinterpret_cast<float*>(base);
-    p.ws_ml = reinterpret_cast<float*>(base + parts * d * sizeof(float));
-    size_t off = parts * d * sizeof(float) + parts * 2 * sizeof(float);
-    off = (off + 255) & ~static_cast<size_t>(255);
-    p.ws_cnt = reinterpret_cast<int32_t*>(base + off);
+    p.ws_cnt = reinterpret_cast<int32_t*>(base);
+    p.ws_o = reinterpret_cast<float*>(base + ta::kCounterSlabBytes);
+    p.ws_ml = reinterpret_cast<float*>(base + ta::kCounterSlabBytes + parts * d * sizeof(float));
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = pl.kernel == 2 ? ta::launch_attn_mfma(p, s) : ta::launch_attn_generic(p, dtype, s);

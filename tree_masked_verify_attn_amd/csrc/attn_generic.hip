@@ -276,10 +276,9 @@ hipError_t launch_attn_generic(const AttnParams& p, int dtype, hipStream_t s) {
 size_t attn_ws_bytes(int tiles, int n_split, int rows_per_tile, int d) {
   if (n_split <= 1) return 0;
   const size_t parts = static_cast<size_t>(tiles) * n_split * rows_per_tile;
-  size_t bytes = parts * d * sizeof(float);        // ws_o
+  size_t bytes = kCounterSlabBytes;                // arrival counters, always at offset 0
+  bytes += parts * d * sizeof(float);              // ws_o
   bytes += parts * 2 * sizeof(float);              // ws_ml
-  bytes = (bytes + 255) & ~static_cast<size_t>(255);
-  bytes += static_cast<size_t>(tiles) * sizeof(int32_t);  // counters
   return bytes;
 }
 

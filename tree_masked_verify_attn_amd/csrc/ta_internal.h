@@ -38,7 +38,12 @@ struct AttnParams {
   int32_t* ws_cnt;      // [tiles] arrival counters (zero between calls)
 };
 
-// Workspace layout for a plan; returns bytes.
+// Workspace layout: a fixed slab of arrival counters at offset 0 (so that
+// counters never overlap partial results of a differently sized earlier
+// call), then the partial outputs, then the (max, sum) pairs.
+constexpr size_t kCounterSlabBytes = 64 * 1024;
+constexpr int kMaxTiles = static_cast<int>(kCounterSlabBytes / sizeof(int32_t));
+// Returns the bytes needed for a plan (0 when there is a single split).
 size_t attn_ws_bytes(int tiles, int n_split, int rows_per_tile, int d);
 
 hipError_t launch_attn_generic(const AttnParams& p, int dtype, hipStream_t s);
