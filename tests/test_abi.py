@@ -111,3 +111,15 @@ def test_workspace_query_rejects_bad_sizes():
     with pytest.raises(ta.TreeAttnError):
         ta.tree_attn_workspace_bytes(1, 4, 6, 4, 128, ta.TA_BF16, 100)
     assert ta.tree_attn_workspace_bytes(0, 4, 8, 4, 128, ta.TA_BF16, 100) == 0
+
+
+def test_binding_refuses_host_memory_for_device_arguments():
+    """Host tensors never reach the library as device pointers."""
+    import torch
+    ws = ta.Workspace()
+    with pytest.raises(ValueError):
+        ws.get(1024, "cpu")
+    with pytest.raises(ValueError):
+        _lib._need(torch.zeros(4), "workspace")
+    with pytest.raises(ValueError):
+        ta.KVCache(torch.zeros(1, 4, 1, 64), torch.zeros(1, 4, 1, 64))

@@ -222,12 +222,19 @@ class Workspace:
         self.device = device
         self.buf = None
 
-    def get(self, nbytes: int):
+    def get(self, nbytes: int, device=None):
+        """The buffer (at least ``nbytes``) on ``device`` (default: the one given at
+        construction); always device memory, never host memory."""
         torch = _torch()
         if nbytes == 0:
             return None
-        if self.buf is None or self.buf.numel() < nbytes:
-            self.buf = torch.zeros(nbytes + 256, dtype=torch.uint8, device=self.device)
+        dev = torch.device(device if device is not None else self.device)
+        if dev.type != "cuda":
+            raise ValueError("a workspace must live in GPU memory")
+        if dev.index is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
+        if self.buf is None or self.buf.numel() < nbytes or self.buf.device != dev:
+            self.buf = torch.zeros(nbytes + 256, dtype=torch.uint8, device=dev)
         return self.buf
 
 
@@ -278,7 +285,9 @@ def _attention(fn_name, q, kv: KVCache, prefix_len, parent, n_nodes, scale, out,
     if workspace is None:
         ws = _workspace_for(dev, nbytes)
     else:
-        ws = workspace.get(nbytes) if isinstance(workspace, Workspace) else workspace
+        ws = workspace.get(nbytes, dev) if isinstance(workspace, Workspace) else workspace
+    if ws is not None:
+        _need(ws, "workspace", device=dev)   # device memory of this call's GPU only
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     common = (q.data_ptr(), kv.struct(), prefix_len.data_ptr(), parent.data_ptr(),
               n_nodes.data_ptr())
@@ -330,6 +339,11 @@ def accept_greedy_path(logits, parent, tok, n_nodes, root_tok, path=None, path_l
         path_len = torch.empty((B,), dtype=torch.int32, device=dev)
     if bonus is None:
         bonus = torch.empty((B,), dtype=torch.int32, device=dev)
+    _need(path, "path", dtype=torch.int32, ndim=2, device=dev)
+    _need(path_len, "path_len", dtype=torch.int32, ndim=1, device=dev)
+    _need(bonus, "bonus", dtype=torch.int32, ndim=1, device=dev)
+    if tuple(path.shape) != (B, n_max) or path_len.shape[0] != B or bonus.shape[0] != B:
+        raise ValueError("path must be [B][n_max], path_len and bonus [B]")
     st = lib.accept_greedy_path(logits.data_ptr(), _dtype_code(logits), parent.data_ptr(),
                                 tok.data_ptr(), n_nodes.data_ptr(), root_tok.data_ptr(), B, n_max,
                                 V, path.data_ptr(), path_len.data_ptr(), bonus.data_ptr(),
