@@ -82,6 +82,32 @@ def test_random_verify(ta, case):
     _check_unwritten(O, L, c, lambda n: range(c.n_max))
 
 
+BOTH_KERNELS = [
+    # (seed, B, Hq, Hkv, d, P_range, n_max, target_side, paged, chunk)
+    (21, 3, 8, 1, 128, (0, 700), 16, True, False, 128),     # 128 rows: 4 row groups
+    (22, 4, 16, 2, 128, (50, 900), 8, True, False, 0),      # 64 rows: 2 groups x 2 token halves
+    (23, 5, 64, 8, 128, (10, 600), 6, True, True, 128),     # 48 rows, paged
+    (24, 2, 32, 8, 128, (0, 400), 8, False, False, 256),    # 32 rows: 4 token quarters
+    (25, 3, 12, 1, 64, (0, 500), 8, False, False, 64),      # 96 rows: 3 groups, d = 64
+    (26, 2, 16, 1, 128, (100, 300), 20, False, True, 0),    # 320 rows: 3 row tiles
+]
+
+
+@pytest.mark.parametrize("case", BOTH_KERNELS, ids=[f"seed{c[0]}" for c in BOTH_KERNELS])
+@pytest.mark.parametrize("kernel", [1, 2])
+def test_bf16_both_kernels(ta, case, kernel):
+    seed, B, Hq, Hkv, d, P_range, n_max, target_side, paged, chunk = case
+    c = random_case(seed, B, Hq, Hkv, d, P_range=P_range, n_max=n_max, dtype="bf16",
+                    target_side=target_side, paged=paged)
+    print(f"case seed={seed} kernel={kernel} rows={n_max * Hq // Hkv} d={d} paged={paged}",
+          flush=True)
+    dc = DevCase(c)
+    O, L = _run_verify(ta, dc, chunk, kernel)
+    Or, Lr = oracle.verify(c)
+    assert_attn_close(O, L, Or, Lr, "bf16", what=f"seed{seed} kernel{kernel}")
+    _check_unwritten(O, L, c, lambda n: range(c.n_max))
+
+
 @pytest.mark.parametrize("w", [1, 3, 8])
 def test_random_expand(ta, w):
     import torch

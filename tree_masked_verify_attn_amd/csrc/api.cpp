@@ -51,12 +51,13 @@ bool make_plan(int B, int n_q, int Hq, int Hkv, int d, int dtype, int T_cap,
   const int G = Hq / Hkv;
   const int R = n_q * G;
   int kernel = opts ? opts->kernel : 0;
-  const bool mfma_ok = dtype == TA_BF16 && (d == 128 || d == 64) && false;
+  const bool mfma_ok = dtype == TA_BF16 && (d == 128 || d == 64);
   if (kernel == 0) kernel = mfma_ok ? 2 : 1;
   if (kernel == 2 && !mfma_ok) return false;
   if (kernel != 1 && kernel != 2) return false;
   pl.kernel = kernel;
-  pl.rows_per_tile = kernel == 2 ? kMfmaRows : kGenericRows;
+  // MFMA tiles hold 32 x NRG rows (NRG = 1..4 row groups of 32).
+  pl.rows_per_tile = kernel == 2 ? std::min(kMfmaRows, round_up(R, 32)) : kGenericRows;
   pl.n_row_tiles = (R + pl.rows_per_tile - 1) / pl.rows_per_tile;
   const long long items = static_cast<long long>(B) * Hkv * pl.n_row_tiles;
   int chunk = opts ? opts->chunk_tokens : 0;
@@ -68,7 +69,10 @@ bool make_plan(int B, int n_q, int Hq, int Hkv, int d, int dtype, int T_cap,
     chunk = round_up(static_cast<int>((T_cap + splits - 1) / splits), 64);
     chunk = std::max(chunk, 256);
   }
-  chunk = std::max(64, std::min(chunk, round_up(std::max(T_cap, 1), 64)));
+  // MFMA tiles span 128 positions when a tile has a single row group.
+  const int gran = (kernel == 2 && pl.rows_per_tile == 32) ? 128 : 64;
+  if (chunk % gran != 0) chunk = round_up(chunk, gran);
+  chunk = std::max(gran, std::min(chunk, round_up(std::max(T_cap, 1), gran)));
   pl.chunk = chunk;
   pl.n_split = (T_cap + chunk - 1) / chunk;
   if (pl.n_split < 1) pl.n_split = 1;
