@@ -184,6 +184,11 @@ const char* ta_status_string(int status);
 /* Library version, e.g. "0.1.0" (static string). */
 const char* ta_version(void);
 
+/* The HIP error behind the calling thread's most recent TA_ERR_HIP, as
+ * "<where>: <hip error name> (<description>)"; "" if there was none.  The
+ * string is thread-local and valid until the thread's next failing call. */
+const char* ta_last_error(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
     Workspace,
     accept_greedy_path,
     load_library,
+    ta_last_error,
     ta_status_string,
     ta_version,
     tree_attn_expand,

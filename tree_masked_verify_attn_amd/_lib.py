@@ -34,6 +34,7 @@ EXPORTED_SYMBOLS = (
     "tree_cache_reroot",
     "ta_status_string",
     "ta_version",
+    "ta_last_error",
 )
 
 
@@ -94,13 +95,18 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.ta_status_string.restype = ctypes.c_char_p
         lib.ta_version.argtypes = []
         lib.ta_version.restype = ctypes.c_char_p
+        lib.ta_last_error.argtypes = []
+        lib.ta_last_error.restype = ctypes.c_char_p
         _lib = lib
         return lib
 
 
 def _check(status: int):
     if status != TA_OK:
-        msg = load_library().ta_status_string(status).decode()
+        lib = load_library()
+        msg = lib.ta_status_string(status).decode()
+        if status == TA_ERR_HIP:
+            msg += ": " + lib.ta_last_error().decode()
         raise TreeAttnError(status, msg)
 
 
@@ -110,6 +116,10 @@ def ta_status_string(status: int) -> str:
 
 def ta_version() -> str:
     return load_library().ta_version().decode()
+
+
+def ta_last_error() -> str:
+    return load_library().ta_last_error().decode()
 
 
 # ----------------------------------------------------------------------------

@@ -186,15 +186,12 @@ hipError_t launch_accept(const void* logits, int logit_dtype, const int32_t* par
                          int B, int n_max, int V, int32_t* path, int32_t* path_len,
                          int32_t* bonus, hipStream_t s) {
   dim3 g1(n_max, B);
-  if (logit_dtype == TA_BF16)
-    argmax_kernel<true><<<g1, kThreads, 0, s>>>(logits, n_nodes, n_max, V, path);
-  else
-    argmax_kernel<false><<<g1, kThreads, 0, s>>>(logits, n_nodes, n_max, V, path);
-  hipError_t e = hipGetLastError();
+  hipError_t e = logit_dtype == TA_BF16
+                     ? launch(argmax_kernel<true>, g1, dim3(kThreads), s, logits, n_nodes, n_max, V, path)
+                     : launch(argmax_kernel<false>, g1, dim3(kThreads), s, logits, n_nodes, n_max, V, path);
   if (e != hipSuccess) return e;
-  accept_path_kernel<<<B, kThreads, 0, s>>>(parent, tok, n_nodes, root_tok, n_max, path, path_len,
-                                            bonus);
-  return hipGetLastError();
+  return launch(accept_path_kernel, dim3(B), dim3(kThreads), s, parent, tok, n_nodes, root_tok,
+                n_max, path, path_len, bonus);
 }
 
 }  // namespace ta

@@ -4,13 +4,30 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <cstdio>
 
 #include "ta_internal.h"
 #include "tree_attn.h"
 
+namespace ta {
+namespace {
+thread_local char g_last_error[256] = "";
+}  // namespace
+void set_last_error(hipError_t e, const char* where) {
+  std::snprintf(g_last_error, sizeof(g_last_error), "%s: %s (%s)", where, hipGetErrorName(e),
+                hipGetErrorString(e));
+}
+}  // namespace ta
+
 namespace {
 
 using ta::AttnParams;
+
+int hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return TA_OK;
+  ta::set_last_error(e, where);
+  return TA_ERR_HIP;
+}
 
 int device_cu_count() {
   // Compute units of the current device (cached per device id).
@@ -163,7 +180,8 @@ int run_attention(const void* q, ta_kv kv, const int32_t* prefix_len, const int3
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = pl.kernel == 2 ? ta::launch_attn_mfma(p, s) : ta::launch_attn_generic(p, dtype, s);
-  return e == hipSuccess ? TA_OK : TA_ERR_HIP;
+  return hip_status(e, pl.kernel == 2 ? "attention (MFMA kernel) launch"
+                                      : "attention (generic kernel) launch");
 }
 
 }  // namespace
@@ -209,7 +227,7 @@ int accept_greedy_path(const void* logits, int logit_dtype, const int32_t* paren
   if (B == 0) return TA_OK;
   hipError_t e = ta::launch_accept(logits, logit_dtype, parent, tok, n_nodes, root_tok, B, n_max,
                                    V, path, path_len, bonus, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? TA_OK : TA_ERR_HIP;
+  return hip_status(e, "accept_greedy_path launch");
 }
 
 int tree_cache_reroot(const ta_kv* kv_layers, int n_layers, int32_t* prefix_len, int32_t* parent,
@@ -241,11 +259,11 @@ int tree_cache_reroot(const ta_kv* kv_layers, int n_layers, int32_t* prefix_len,
     }
     hipError_t e = ta::launch_reroot_move(L, cnt, prefix_len, parent, n_nodes, path, path_len,
                                           keep_subtree, B, n_max, Hkv, row_bytes, s);
-    if (e != hipSuccess) return TA_ERR_HIP;
+    if (e != hipSuccess) return hip_status(e, "tree_cache_reroot move launch");
   }
   hipError_t e = ta::launch_reroot_meta(prefix_len, parent, n_nodes, path, path_len, keep_subtree,
                                         B, n_max, s);
-  return e == hipSuccess ? TA_OK : TA_ERR_HIP;
+  return hip_status(e, "tree_cache_reroot metadata launch");
 }
 
 const char* ta_status_string(int status) {
@@ -261,5 +279,7 @@ const char* ta_status_string(int status) {
 }
 
 const char* ta_version(void) { return "0.1.0"; }
+
+const char* ta_last_error(void) { return ta::g_last_error; }
 
 }  // extern "C"

@@ -259,18 +259,11 @@ __global__ __launch_bounds__(kThreads) void attn_generic_kernel(AttnParams p) {
 hipError_t launch_attn_generic(const AttnParams& p, int dtype, hipStream_t s) {
   dim3 grid(p.n_split, p.n_row_tiles, p.B * p.Hkv);
   dim3 block(kThreads);
-  if (dtype == TA_F32) {
-    if (p.d == 64)
-      attn_generic_kernel<float, 64><<<grid, block, 0, s>>>(p);
-    else
-      attn_generic_kernel<float, 128><<<grid, block, 0, s>>>(p);
-  } else {
-    if (p.d == 64)
-      attn_generic_kernel<uint16_t, 64><<<grid, block, 0, s>>>(p);
-    else
-      attn_generic_kernel<uint16_t, 128><<<grid, block, 0, s>>>(p);
-  }
-  return hipGetLastError();
+  if (dtype == TA_F32)
+    return p.d == 64 ? launch(attn_generic_kernel<float, 64>, grid, block, s, p)
+                     : launch(attn_generic_kernel<float, 128>, grid, block, s, p);
+  return p.d == 64 ? launch(attn_generic_kernel<uint16_t, 64>, grid, block, s, p)
+                   : launch(attn_generic_kernel<uint16_t, 128>, grid, block, s, p);
 }
 
 size_t attn_ws_bytes(int tiles, int n_split, int rows_per_tile, int d) {

@@ -411,14 +411,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnParams p) {
 template <int D>
 hipError_t launch_d(const AttnParams& p, hipStream_t s) {
   dim3 grid(p.n_split, p.n_row_tiles, p.B * p.Hkv);
+  const dim3 block(kThreads);
   switch (p.rows_per_tile / 32) {
-    case 1: attn_mfma_kernel<D, 1><<<grid, kThreads, 0, s>>>(p); break;
-    case 2: attn_mfma_kernel<D, 2><<<grid, kThreads, 0, s>>>(p); break;
-    case 3: attn_mfma_kernel<D, 3><<<grid, kThreads, 0, s>>>(p); break;
-    case 4: attn_mfma_kernel<D, 4><<<grid, kThreads, 0, s>>>(p); break;
+    case 1: return launch(attn_mfma_kernel<D, 1>, grid, block, s, p);
+    case 2: return launch(attn_mfma_kernel<D, 2>, grid, block, s, p);
+    case 3: return launch(attn_mfma_kernel<D, 3>, grid, block, s, p);
+    case 4: return launch(attn_mfma_kernel<D, 4>, grid, block, s, p);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace

@@ -189,17 +189,15 @@ hipError_t launch_reroot_move(const RerootLayers& layers, int n_layers, const in
                               const int32_t* path_len, const uint8_t* keep, int B, int n_max,
                               int Hkv, int row_bytes, hipStream_t s) {
   dim3 grid(Hkv, 2, B * n_layers);
-  reroot_move_kernel<<<grid, kThreads, 0, s>>>(layers, n_layers, prefix_len, parent, n_nodes,
-                                               path, path_len, keep, n_max, Hkv, row_bytes);
-  return hipGetLastError();
+  return launch(reroot_move_kernel, grid, dim3(kThreads), s, layers, n_layers, prefix_len, parent,
+                n_nodes, path, path_len, keep, n_max, Hkv, row_bytes);
 }
 
 hipError_t launch_reroot_meta(int32_t* prefix_len, int32_t* parent, int32_t* n_nodes,
                               const int32_t* path, const int32_t* path_len, const uint8_t* keep,
                               int B, int n_max, hipStream_t s) {
-  reroot_meta_kernel<<<B, kThreads, 0, s>>>(prefix_len, parent, n_nodes, path, path_len, keep,
-                                            n_max);
-  return hipGetLastError();
+  return launch(reroot_meta_kernel, dim3(B), dim3(kThreads), s, prefix_len, parent, n_nodes, path,
+                path_len, keep, n_max);
 }
 
 }  // namespace ta

@@ -5,9 +5,34 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <type_traits>
+#include <utility>
+
 #include "tree_attn.h"
 
 namespace ta {
+
+// Launches `kernel` and returns the status of this launch only (unlike
+// hipGetLastError, which also reports errors left behind by other code).
+template <typename Tuple, size_t... I>
+inline hipError_t launch_tuple(const void* kernel, dim3 grid, dim3 block, hipStream_t s,
+                               Tuple& vals, std::index_sequence<I...>) {
+  void* ptrs[] = {static_cast<void*>(&std::get<I>(vals))..., nullptr};
+  return hipLaunchKernel(kernel, grid, block, ptrs, 0, s);
+}
+template <typename... Params, typename... Args>
+inline hipError_t launch(void (*kernel)(Params...), dim3 grid, dim3 block, hipStream_t s,
+                         Args&&... args) {
+  static_assert(sizeof...(Params) == sizeof...(Args), "kernel argument count");
+  // converted to the kernel's own parameter types before their addresses are taken
+  std::tuple<std::decay_t<Params>...> vals(std::forward<Args>(args)...);
+  return launch_tuple(reinterpret_cast<const void*>(kernel), grid, block, s, vals,
+                      std::index_sequence_for<Params...>{});
+}
+
+// Records the last HIP failure of the calling thread (read by ta_last_error).
+void set_last_error(hipError_t e, const char* where);
 
 // ---------------------------------------------------------------------------
 // Plain-old-data parameter block of one attention launch (passed by value).
