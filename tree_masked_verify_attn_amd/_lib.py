@@ -74,6 +74,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             raise RuntimeError(
                 f"{path} is missing: build the HIP library first "
                 "(python -m tree_masked_verify_attn_amd.build)")
+        # torch brings its own HIP runtime (soname libamdhip64.so.7, requested by
+        # torch under another name).  Loading torch first makes libtreeattn bind
+        # to that same runtime by soname; the other order would put two HIP
+        # runtimes in the process, and the second one finds no device.
+        import torch  # noqa: F401
         lib = ctypes.CDLL(path)
         c_int, c_size, vp, f32 = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
         lib.tree_attn_workspace_bytes.argtypes = [c_int] * 7 + [ctypes.POINTER(ta_attn_opts)]
