@@ -90,15 +90,16 @@ BOTH_KERNELS = [
     (24, 2, 32, 8, 128, (0, 400), 8, False, False, 256),    # 32 rows: 4 token quarters
     (25, 3, 12, 1, 64, (0, 500), 8, False, False, 64),      # 96 rows: 3 groups, d = 64
     (26, 2, 16, 1, 128, (100, 300), 20, False, True, 0),    # 320 rows: 3 row tiles
+    (27, 2, 8, 1, 128, (700, 900), 8, True, True, 0),       # paged, 1-position blocks
 ]
 
 
 @pytest.mark.parametrize("case", BOTH_KERNELS, ids=[f"seed{c[0]}" for c in BOTH_KERNELS])
-@pytest.mark.parametrize("kernel", [1, 2])
+@pytest.mark.parametrize("kernel", [1, 2, 3])
 def test_bf16_both_kernels(ta, case, kernel):
     seed, B, Hq, Hkv, d, P_range, n_max, target_side, paged, chunk = case
     c = random_case(seed, B, Hq, Hkv, d, P_range=P_range, n_max=n_max, dtype="bf16",
-                    target_side=target_side, paged=paged)
+                    target_side=target_side, paged=paged, block_size=1 if seed == 27 else 16)
     print(f"case seed={seed} kernel={kernel} rows={n_max * Hq // Hkv} d={d} paged={paged}",
           flush=True)
     dc = DevCase(c)

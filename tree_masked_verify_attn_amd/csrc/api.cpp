@@ -49,7 +49,7 @@ constexpr int kGenericRows = 32;
 constexpr int kMfmaRows = 128;  // query rows (G x nodes) per MFMA work group, at most
 
 struct Plan {
-  int kernel;         // 1 generic, 2 mfma
+  int kernel;         // 1 generic, 2 MFMA (register prefetch), 3 MFMA (LDS-DMA ring)
   int rows_per_tile;
   int n_row_tiles;
   int chunk;
@@ -70,11 +70,13 @@ bool make_plan(int B, int n_q, int Hq, int Hkv, int d, int dtype, int T_cap,
   int kernel = opts ? opts->kernel : 0;
   const bool mfma_ok = dtype == TA_BF16 && (d == 128 || d == 64);
   if (kernel == 0) kernel = mfma_ok ? 2 : 1;
-  if (kernel == 2 && !mfma_ok) return false;
-  if (kernel != 1 && kernel != 2) return false;
+  if ((kernel == 2 || kernel == 3) && !mfma_ok) return false;
+  if (kernel < 1 || kernel > 3) return false;
   pl.kernel = kernel;
-  // MFMA tiles hold 32 x NRG rows (NRG = 1..4 row groups of 32).
-  pl.rows_per_tile = kernel == 2 ? std::min(kMfmaRows, round_up(R, 32)) : kGenericRows;
+  // Both MFMA kernels share one plan (so they need the same workspace): tiles
+  // hold 32 x NRG rows (NRG = 1..4 row groups of 32).
+  const bool mfma = kernel != 1;
+  pl.rows_per_tile = mfma ? std::min(kMfmaRows, round_up(R, 32)) : kGenericRows;
   pl.n_row_tiles = (R + pl.rows_per_tile - 1) / pl.rows_per_tile;
   const long long items = static_cast<long long>(B) * Hkv * pl.n_row_tiles;
   int chunk = opts ? opts->chunk_tokens : 0;
@@ -87,7 +89,7 @@ bool make_plan(int B, int n_q, int Hq, int Hkv, int d, int dtype, int T_cap,
     chunk = std::max(chunk, 256);
   }
   // MFMA tiles span 128 positions when a tile has a single row group.
-  const int gran = (kernel == 2 && pl.rows_per_tile == 32) ? 128 : 64;
+  const int gran = (mfma && pl.rows_per_tile == 32) ? 128 : 64;
   if (chunk % gran != 0) chunk = round_up(chunk, gran);
   chunk = std::max(gran, std::min(chunk, round_up(std::max(T_cap, 1), gran)));
   pl.chunk = chunk;
@@ -138,8 +140,13 @@ int run_attention(const void* q, ta_kv kv, const int32_t* prefix_len, const int3
   if (B == 0) return TA_OK;
   Plan pl;
   if (!make_plan(B, n_q, Hq, Hkv, d, dtype, kv.T_cap, opts, pl)) return TA_ERR_UNSUPPORTED;
-  if (pl.kernel == 2 && !(aligned16(q) && aligned16(out) && aligned16(kv.k) && aligned16(kv.v)))
+  if (pl.kernel != 1 && !(aligned16(q) && aligned16(out) && aligned16(kv.k) && aligned16(kv.v)))
     return TA_ERR_INVALID_ARG;
+  // The streaming kernel keeps one split's paged block ids in LDS; when they do
+  // not fit it hands the call to the other MFMA kernel (same plan, same workspace).
+  if (pl.kernel == 3 && kv.block_table != nullptr &&
+      pl.chunk / kv.block_size + 2 > ta::kStreamMaxSplitBlocks)
+    pl.kernel = 2;
   if (pl.ws_bytes > 0 && (ws == nullptr || ws_bytes < pl.ws_bytes || !aligned16(ws)))
     return TA_ERR_WORKSPACE;
 
@@ -179,9 +186,19 @@ int run_attention(const void* q, ta_kv kv, const int32_t* prefix_len, const int3
     p.ws_ml = reinterpret_cast<float*>(base + ta::kCounterSlabBytes + parts * d * sizeof(float));
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = pl.kernel == 2 ? ta::launch_attn_mfma(p, s) : ta::launch_attn_generic(p, dtype, s);
-  return hip_status(e, pl.kernel == 2 ? "attention (MFMA kernel) launch"
-                                      : "attention (generic kernel) launch");
+  hipError_t e;
+  const char* where;
+  if (pl.kernel == 3) {
+    e = ta::launch_attn_stream(p, 4, s);
+    where = "attention (streaming MFMA kernel) launch";
+  } else if (pl.kernel == 2) {
+    e = ta::launch_attn_mfma(p, s);
+    where = "attention (MFMA kernel) launch";
+  } else {
+    e = ta::launch_attn_generic(p, dtype, s);
+    where = "attention (generic kernel) launch";
+  }
+  return hip_status(e, where);
 }
 
 }  // namespace

@@ -1,0 +1,412 @@
+// bf16 tree-masked verify/expand attention, streaming variant for gfx950.
+//
+// Same mathematics and the same MFMA formulation as attn_mfma.hip (S^T = K .
+// Q^T and O^T = V^T . P^T on v_mfma_f32_32x32x16_bf16, one query row per lane
+// pair, lazy rescale, ancestor bitmask only on the tile that reaches the tree
+// cache; SwiftSpec summary, Section 3.1.3 Figure 3 and Section 3.2), but built
+// to keep many KV bytes in flight per compute unit:
+//  * K/V move from HBM straight into a ring of S LDS stages of 32 positions
+//    with global_load_lds_dwordx4 (no staging registers).  Lane i of a load
+//    fetches the global 16-byte chunk that belongs at LDS position
+//    base + 16 * i of the XOR-swizzled layout.
+//  * The loads are issued from inline assembly and waited for with explicit
+//    s_waitcnt vmcnt(N) + s_barrier, so the compiler cannot add a blanket
+//    vmcnt(0) in front of every LDS read: S-1 stages stay in flight while one
+//    is consumed.
+//  * Each computing wave owns one 32-row group of the tile's rows and
+//    consumes every stage; waves beyond the row groups only issue loads.
+//  * Paged caches: the split's block ids are copied to LDS first, so the
+//    ring loop issues no other vector-memory loads.
+//  * Splits merge in the same launch (last arriving work group).
+#include "ta_device.h"
+
+namespace ta {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+constexpr int kThreads = 256;
+constexpr int kTile = 32;             // KV positions per ring stage
+constexpr float kRescaleSlack = 8.f;  // log2 units
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr int kMaxSplitBlocks = 512;  // paged: block ids of one split cached in LDS
+
+template <int D>
+__device__ __forceinline__ int swz(int t) {
+  const int h = ((t & 3) << 1) | ((t >> 2) & 1);
+  return D == 128 ? (h | (((t >> 3) & 1) << 3)) : h;
+}
+template <int D>
+__device__ __forceinline__ int lds_off(int t, int chunk) {  // bytes within a K or V stage
+  return t * (D * 2) + ((chunk ^ swz<D>(t)) << 4);
+}
+
+__device__ __forceinline__ float lane_swap32(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float((threadIdx.x & 63) < 32 ? r[1] : r[0]);
+}
+
+// 64 lanes x 16 bytes from `g` (per lane) into LDS [lds_base, lds_base + 1 KiB).
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds_base), "v"(g)
+               : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+// Workgroup barrier without the fence of __syncthreads (which would wait for
+// every outstanding load); the wave's own LDS reads are complete first.
+__device__ __forceinline__ void raw_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
+}
+
+template <int D, int NRG, int S>
+struct SCfg {
+  static constexpr int CH = D / 8;                  // 16-byte chunks per row
+  static constexpr int ROW = D * 2;                 // bytes per row
+  static constexpr int HALF = kTile * ROW;          // K (or V) bytes per stage
+  static constexpr int STAGE = 2 * HALF;
+  static constexpr int ROWS_PER_INST = 1024 / ROW;  // rows one 1 KiB load covers
+  static constexpr int INST_PER_WAVE = HALF / 1024 / 4;  // per wave, for K (same for V)
+  static constexpr int NL = 2 * INST_PER_WAVE;      // loads per thread per stage
+  static constexpr int KS = D / 16;
+  static constexpr int MB = D / 32;
+  static constexpr int RPT = 32 * NRG;
+  static constexpr int RING = S * STAGE;
+  static constexpr int SETUP = kMaxNodes * kMaskWords * 8 + kMaxNodes * 4;  // anc + jump
+  static constexpr int LDS = RING > SETUP ? RING : SETUP;
+};
+
+template <int N, int NL>
+__device__ __forceinline__ void wait_stage(int pending_after) {
+  // pending_after = stages issued after the one we need (0 .. N)
+  if constexpr (N >= 3) {
+    if (pending_after >= 3) { wait_vmcnt<3 * NL>(); return; }
+  }
+  if constexpr (N >= 2) {
+    if (pending_after >= 2) { wait_vmcnt<2 * NL>(); return; }
+  }
+  if (pending_after >= 1) { wait_vmcnt<NL>(); return; }
+  wait_vmcnt<0>();
+}
+
+template <int D, int NRG, int S>
+__global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) {
+  using C = SCfg<D, NRG, S>;
+  static_assert(S >= 2 && S <= 4, "ring depth");
+  __shared__ __attribute__((aligned(1024))) uint8_t sRing[C::LDS];
+  __shared__ int sBlk[kMaxSplitBlocks];
+  __shared__ int sLast;
+
+  const int split = blockIdx.x;
+  const int rtile = blockIdx.y;
+  const int bh = blockIdx.z;
+  const int b = bh / p.Hkv;
+  const int hkv = bh % p.Hkv;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int lhi = lane >> 5;
+  const int l32 = lane & 31;
+
+  SeqBounds sb;
+  if (!seq_bounds(p.prefix_len, p.n_nodes, b, p.n_max, p.T_cap, sb)) return;
+  const int nsplit = (sb.T + p.chunk - 1) / p.chunk;
+  if (split >= nsplit) return;
+  const int t_begin = split * p.chunk;
+  const int t_end = min(sb.T, t_begin + p.chunk);
+
+  const int rg = wave < NRG ? wave : -1;  // computing waves own one 32-row group each
+  const int R = p.n_q * p.G;
+  const int row_in_tile = (rg < 0 ? 0 : rg) * 32 + l32;
+  const int grow = rtile * C::RPT + row_in_tile;
+  int node = -1, slot = 0, g = 0;
+  if (rg >= 0 && grow < R) {
+    slot = grow / p.G;
+    g = grow % p.G;
+    node = p.expand ? sb.n - p.n_q + slot : slot;
+    if (node < 0 || node >= sb.n) node = -1;
+  }
+  if (!__syncthreads_or(node >= 0)) return;
+
+  // ---- setup: ancestor masks (in the ring's space), paged block ids ------------
+  const bool has_tree = t_end > sb.P;
+  uint64_t anc[kMaskWords] = {0, 0, 0, 0};
+  {
+    auto sAnc = reinterpret_cast<uint64_t(*)[kMaskWords]>(sRing);
+    int* sJump = reinterpret_cast<int*>(sRing + kMaxNodes * kMaskWords * 8);
+    if (has_tree) build_ancestor_masks(p.parent + static_cast<size_t>(b) * p.n_max, sb.n, sAnc, sJump);
+    if (p.block_table != nullptr) {
+      const int blk0 = t_begin / p.block_size;
+      const int nblk = (t_end - 1) / p.block_size - blk0 + 1;  // <= kMaxSplitBlocks (planner)
+      for (int i = tid; i < nblk && i < kMaxSplitBlocks; i += kThreads) {
+        int v = p.block_table[static_cast<size_t>(b) * p.max_blocks + blk0 + i];
+        sBlk[i] = v < 0 ? 0 : (v >= p.num_blocks ? p.num_blocks - 1 : v);
+      }
+    }
+    __syncthreads();
+    if (has_tree && node >= 0) {
+#pragma unroll
+      for (int w = 0; w < kMaskWords; ++w) anc[w] = sAnc[node][w];
+    }
+    __syncthreads();  // the ring may now overwrite the masks
+  }
+
+  const uint16_t* Q = static_cast<const uint16_t*>(p.q);
+  const size_t qrow = ((static_cast<size_t>(b) * p.n_q + slot) * p.Hq + hkv * p.G + g) * D;
+  bf16x8 qreg[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (node >= 0) v = *reinterpret_cast<const u32x4*>(Q + qrow + (2 * ks + lhi) * 8);
+    qreg[ks] = __builtin_bit_cast(bf16x8, v);
+  }
+  // Complete the Q loads with a wait the compiler can see (vmcnt(0), other
+  // counters untouched); otherwise it would re-wait for them inside the ring
+  // loop, where the outstanding loads are the ring's.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+
+  // ---- ring of stages ----------------------------------------------------
+  const uint8_t* Kg = static_cast<const uint8_t*>(p.k);
+  const uint8_t* Vg = static_cast<const uint8_t*>(p.v);
+  const uint32_t ring_base = static_cast<uint32_t>(reinterpret_cast<size_t>((lds_u8*)sRing));
+  const int ntiles = (t_end - t_begin + kTile - 1) / kTile;
+  const int blk0 = p.block_table != nullptr ? t_begin / p.block_size : 0;
+
+  // Byte offset of row `tok` (clamped into the split) of the K or V cache.
+  auto row_bytes_off = [&](int tok) -> size_t {
+    tok = tok < t_end ? tok : t_end - 1;
+    size_t row;
+    if (p.block_table != nullptr) {
+      const int blk = sBlk[tok / p.block_size - blk0];
+      row = (static_cast<size_t>(blk) * p.block_size + tok % p.block_size) * p.Hkv + hkv;
+    } else {
+      row = (static_cast<size_t>(b) * p.T_cap + tok) * p.Hkv + hkv;
+    }
+    return row * C::ROW;
+  };
+  auto issue_stage = [&](int j) {
+    const int tb = t_begin + j * kTile;
+    const uint32_t sbase = ring_base + (j % S) * C::STAGE;
+#pragma unroll
+    for (int q = 0; q < C::INST_PER_WAVE; ++q) {
+      const int r0 = (wave * C::INST_PER_WAVE + q) * C::ROWS_PER_INST;
+      const int r = r0 + lane / C::CH;
+      const int pc = lane % C::CH;
+      const int c = pc ^ swz<D>(r);
+      const size_t off = row_bytes_off(tb + r) + c * 16;
+      const uint32_t lk = __builtin_amdgcn_readfirstlane(sbase + r0 * C::ROW);
+      dma16(Kg + off, lk);
+      dma16(Vg + off, lk + C::HALF);
+    }
+  };
+
+  f32x16 acc[C::MB];
+#pragma unroll
+  for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[mb][r] = 0.f;
+  float m_ref = -INFINITY;
+  float l_sum = 0.f;
+  const float cs = p.scale_log2;
+  const int lim = min(sb.P, t_end);
+
+  for (int j = 0; j < S - 1 && j < ntiles; ++j) issue_stage(j);
+
+  for (int j = 0; j < ntiles; ++j) {
+    // stage j has landed once at most (stages issued after it) x NL loads are pending
+    wait_stage<S - 2, C::NL>(min(S - 2, ntiles - 1 - j));
+    raw_barrier();  // all waves: stage j visible, stage j-1 no longer read
+    if (j + S - 1 < ntiles) issue_stage(j + S - 1);
+
+    if (rg >= 0) {
+      const int tb = t_begin + j * kTile;
+      const uint8_t* sK = sRing + (j % S) * C::STAGE;
+      const uint8_t* sV = sK + C::HALF;
+      f32x16 Sc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) Sc[r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(sK + lds_off<D>(l32, 2 * ks + lhi));
+        Sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qreg[ks], Sc,
+                                                     0, 0, 0);
+      }
+      if (tb + kTile > lim) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int t = tb + 8 * (r >> 2) + 4 * lhi + (r & 3);
+          bool vis = t < t_end;
+          if (vis && t >= sb.P) {
+            const int jj = t - sb.P;
+            vis = (anc[jj >> 6] >> (jj & 63)) & 1ull;
+          }
+          if (!vis) Sc[r] = -INFINITY;
+        }
+      }
+      float mx = Sc[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, Sc[r]);
+      mx = fmaxf(mx, lane_swap32(mx)) * cs;
+      const bool bump = mx > m_ref + kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(bump) != 0ull) {
+        const float m_new = bump ? mx : m_ref;
+        const float alpha = (m_ref == -INFINITY) ? 0.f : exp2f(m_ref - m_new);
+        l_sum *= alpha;
+#pragma unroll
+        for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[mb][r] *= alpha;
+        m_ref = m_new;
+      }
+      const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+      float rs = 0.f;
+      bf16x8 pk[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pr = exp2f(fmaf(Sc[r], cs, -m_use));
+        rs += pr;
+        pk[r >> 3][r & 7] = static_cast<__bf16>(pr);
+      }
+      l_sum += rs + lane_swap32(rs);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int mb = 0; mb < C::MB; ++mb) {
+          const int gi = lane >> 4, jl = lane & 15;
+          const int d0 = 32 * mb + 16 * (gi & 1);
+          const int trow = 16 * kk + 4 * (gi >> 1) + (jl >> 2);
+          const int dd = d0 + 4 * (jl & 3);
+          const int o1 = lds_off<D>(trow, dd >> 3) + (dd & 7) * 2;
+          const int o2 = lds_off<D>(trow + 8, dd >> 3) + (dd & 7) * 2;
+          const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sV + o1));
+          const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sV + o2));
+          const u32x2 w1 = __builtin_bit_cast(u32x2, v1), w2 = __builtin_bit_cast(u32x2, v2);
+          const u32x4 w = {w1[0], w1[1], w2[0], w2[1]};
+          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pk[kk],
+                                                            acc[mb], 0, 0, 0);
+        }
+      }
+    }
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  uint16_t* Out = static_cast<uint16_t*>(p.out);
+  const size_t orow = ((static_cast<size_t>(b) * p.n_q + slot) * p.Hq + hkv * p.G + g) * D;
+  const size_t lrow = (static_cast<size_t>(b) * p.Hq + hkv * p.G + g) * p.n_q + slot;
+
+  if (nsplit == 1) {
+    if (rg >= 0 && node >= 0) {
+      const float inv = 1.f / l_sum;
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d = 32 * mb + 8 * q4 + 4 * lhi;
+          const uint32_t lo = f32_to_bf16_bits(acc[mb][4 * q4 + 0] * inv) |
+                              (static_cast<uint32_t>(f32_to_bf16_bits(acc[mb][4 * q4 + 1] * inv)) << 16);
+          const uint32_t hi = f32_to_bf16_bits(acc[mb][4 * q4 + 2] * inv) |
+                              (static_cast<uint32_t>(f32_to_bf16_bits(acc[mb][4 * q4 + 3] * inv)) << 16);
+          *reinterpret_cast<u32x2*>(Out + orow + d) = u32x2{lo, hi};
+        }
+      if (p.lse != nullptr && lhi == 0) p.lse[lrow] = (m_ref + log2f(l_sum)) * kLn2;
+    }
+    return;
+  }
+
+  const int tile_id = bh * p.n_row_tiles + rtile;
+  const size_t part = static_cast<size_t>(tile_id) * p.n_split;
+  if (rg >= 0) {
+    float* po = p.ws_o + ((part + split) * C::RPT + row_in_tile) * D;
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = 32 * mb + 8 * q4 + 4 * lhi;
+        *reinterpret_cast<f32x4*>(po + d) =
+            f32x4{acc[mb][4 * q4], acc[mb][4 * q4 + 1], acc[mb][4 * q4 + 2], acc[mb][4 * q4 + 3]};
+      }
+    if (lhi == 0) {
+      p.ws_ml[((part + split) * C::RPT + row_in_tile) * 2 + 0] = m_ref;
+      p.ws_ml[((part + split) * C::RPT + row_in_tile) * 2 + 1] = l_sum;
+    }
+  }
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    const int prev = __hip_atomic_fetch_add(p.ws_cnt + tile_id, 1, __ATOMIC_ACQ_REL,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+    sLast = (prev == nsplit - 1);
+  }
+  __syncthreads();
+  if (!sLast) return;
+  __threadfence();
+
+  constexpr int kGroups = D / 4;
+  for (int e = tid; e < C::RPT * kGroups; e += kThreads) {
+    const int r = e / kGroups, dg = e % kGroups;
+    const int gr = rtile * C::RPT + r;
+    if (gr >= R) continue;
+    const int sl = gr / p.G, gg = gr % p.G;
+    const int nd = p.expand ? sb.n - p.n_q + sl : sl;
+    if (nd < 0 || nd >= sb.n) continue;
+    float M = -INFINITY;
+    for (int s = 0; s < nsplit; ++s)
+      M = fmaxf(M, __builtin_nontemporal_load(p.ws_ml + ((part + s) * C::RPT + r) * 2));
+    float L = 0.f;
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < nsplit; ++s) {
+      const float ms = __builtin_nontemporal_load(p.ws_ml + ((part + s) * C::RPT + r) * 2);
+      const float ls = __builtin_nontemporal_load(p.ws_ml + ((part + s) * C::RPT + r) * 2 + 1);
+      const float wgt = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
+      L = fmaf(ls, wgt, L);
+      const f32x4 ps = __builtin_nontemporal_load(
+          reinterpret_cast<const f32x4*>(p.ws_o + ((part + s) * C::RPT + r) * D + 4 * dg));
+      o += ps * wgt;
+    }
+    const float inv = 1.f / L;
+    const size_t orr = ((static_cast<size_t>(b) * p.n_q + sl) * p.Hq + hkv * p.G + gg) * D + 4 * dg;
+    const uint32_t lo = f32_to_bf16_bits(o[0] * inv) |
+                        (static_cast<uint32_t>(f32_to_bf16_bits(o[1] * inv)) << 16);
+    const uint32_t hi = f32_to_bf16_bits(o[2] * inv) |
+                        (static_cast<uint32_t>(f32_to_bf16_bits(o[3] * inv)) << 16);
+    *reinterpret_cast<u32x2*>(Out + orr) = u32x2{lo, hi};
+    if (p.lse != nullptr && dg == 0)
+      p.lse[(static_cast<size_t>(b) * p.Hq + hkv * p.G + gg) * p.n_q + sl] = (M + log2f(L)) * kLn2;
+  }
+  if (tid == 0)
+    __hip_atomic_store(p.ws_cnt + tile_id, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int D, int S>
+hipError_t launch_ds(const AttnParams& p, hipStream_t s) {
+  const dim3 grid(p.n_split, p.n_row_tiles, p.B * p.Hkv);
+  const dim3 block(kThreads);
+  switch (p.rows_per_tile / 32) {
+    case 1: return launch(attn_stream_kernel<D, 1, S>, grid, block, s, p);
+    case 2: return launch(attn_stream_kernel<D, 2, S>, grid, block, s, p);
+    case 3: return launch(attn_stream_kernel<D, 3, S>, grid, block, s, p);
+    case 4: return launch(attn_stream_kernel<D, 4, S>, grid, block, s, p);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_stream(const AttnParams& p, int stages, hipStream_t s) {
+  if (p.d == 128) return stages == 3 ? launch_ds<128, 3>(p, s) : launch_ds<128, 4>(p, s);
+  if (p.d == 64) return stages == 3 ? launch_ds<64, 3>(p, s) : launch_ds<64, 4>(p, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ta

@@ -73,6 +73,9 @@ size_t attn_ws_bytes(int tiles, int n_split, int rows_per_tile, int d);
 
 hipError_t launch_attn_generic(const AttnParams& p, int dtype, hipStream_t s);
 hipError_t launch_attn_mfma(const AttnParams& p, hipStream_t s);
+// Streaming MFMA variant: `stages` (3 or 4) 32-position LDS stages in flight.
+hipError_t launch_attn_stream(const AttnParams& p, int stages, hipStream_t s);
+constexpr int kStreamMaxSplitBlocks = 512;  // paged: block ids of one split held in LDS
 
 // Accept: argmax pass (writes a[i] into path) then the path pass.
 hipError_t launch_accept(const void* logits, int logit_dtype, const int32_t* parent,
