@@ -149,7 +149,9 @@ def main(argv=None):
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a 1 GiB device copy (for PMC byte-counter scaling)")
-    ap.add_argument("--kernel", type=int, default=0, help="0 auto, 1 generic, 2 MFMA")
+    ap.add_argument("--kernel", type=int, default=0,
+                    help="0 auto, 1 generic, 2 MFMA (register prefetch), 3 MFMA (LDS-DMA ring)")
+    ap.add_argument("--chunk", type=int, default=0, help="KV positions per split (0 = auto)")
     a = ap.parse_args(argv)
 
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -207,7 +209,7 @@ def main(argv=None):
         if marks is not None:
             marks[0].record()
         ta.tree_attn_verify(q, kv, P, par, n, c.scale, out=out, lse=lse, workspace=ws,
-                            kernel=a.kernel)
+                            kernel=a.kernel, chunk_tokens=a.chunk)
         if marks is not None:
             marks[1].record()
         ta.accept_greedy_path(logits, par, tok, n, root_tok, path, plen, bonus)

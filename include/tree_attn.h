@@ -89,13 +89,13 @@ typedef struct {
 
 /*
  * Workspace (bytes) needed by tree_attn_verify / tree_attn_expand for these
- * sizes.  n_q is n_max for verify and w for expand.  The workspace holds a
- * fixed 64 KiB slab of arrival counters at offset 0 followed by split-KV
- * partial results.  It must be zero-filled once before its first use; every
- * call leaves the counter slab at zero again, so one buffer can serve any
- * later call (any sizes, as long as it is large enough) on the same stream.
- * Calls that overlap in time must not share a workspace.  Returns 0 when no
- * split is needed (ws may then be NULL), or (size_t)-1 for invalid sizes.
+ * sizes.  n_q is n_max for verify and w for expand.  The workspace holds the
+ * split-KV partial results (per split and query row: running maximum, sum and
+ * unnormalised output) that a second, combining launch of the same call
+ * reads; its contents need no initialisation and are meaningless between
+ * calls.  Calls that overlap in time must not share a workspace.  Returns 0
+ * when no split is needed (ws may then be NULL), or (size_t)-1 for invalid
+ * sizes.
  */
 size_t tree_attn_workspace_bytes(int B, int n_q, int Hq, int Hkv, int d, int dtype, int T_cap,
                                  const ta_attn_opts* opts);

@@ -225,12 +225,10 @@ def tree_attn_workspace_bytes(B: int, n_q: int, Hq: int, Hkv: int, d: int, dtype
 
 
 class Workspace:
-    """A zero-initialised device buffer reused across attention calls.
+    """A device buffer for split-KV partial results, reused across attention calls.
 
-    The library keeps its arrival counters in a fixed slab at the start of the
-    buffer and leaves them at zero after every call, so the buffer is zeroed
-    only when it is (re)allocated, and any later call may reuse it.  Calls
-    sharing one workspace must be ordered (one stream).
+    It grows when a plan needs more room; its contents need no initialisation.
+    Calls sharing one workspace must be ordered (one stream).
     """
 
     def __init__(self, device=None):
@@ -249,7 +247,7 @@ class Workspace:
         if dev.index is None:
             dev = torch.device("cuda", torch.cuda.current_device())
         if self.buf is None or self.buf.numel() < nbytes or self.buf.device != dev:
-            self.buf = torch.zeros(nbytes + 256, dtype=torch.uint8, device=dev)
+            self.buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)
         return self.buf
 
 

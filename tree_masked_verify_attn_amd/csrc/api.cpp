@@ -96,12 +96,6 @@ bool make_plan(int B, int n_q, int Hq, int Hkv, int d, int dtype, int T_cap,
   pl.n_split = (T_cap + chunk - 1) / chunk;
   if (pl.n_split < 1) pl.n_split = 1;
   const long long tiles = static_cast<long long>(B) * Hkv * pl.n_row_tiles;
-  if (pl.n_split > 1 && tiles > ta::kMaxTiles) {
-    // more work groups than counters: fall back to one split when possible
-    if (opts && opts->chunk_tokens) return false;
-    pl.chunk = round_up(std::max(T_cap, 1), 64);
-    pl.n_split = 1;
-  }
   pl.ws_bytes = ta::attn_ws_bytes(static_cast<int>(tiles), pl.n_split, pl.rows_per_tile, d);
   return true;
 }
@@ -181,9 +175,8 @@ int run_attention(const void* q, ta_kv kv, const int32_t* prefix_len, const int3
     const int tiles = B * Hkv * pl.n_row_tiles;
     const size_t parts = static_cast<size_t>(tiles) * pl.n_split * pl.rows_per_tile;
     uint8_t* base = static_cast<uint8_t*>(ws);
-    p.ws_cnt = reinterpret_cast<int32_t*>(base);
-    p.ws_o = reinterpret_cast<float*>(base + ta::kCounterSlabBytes);
-    p.ws_ml = reinterpret_cast<float*>(base + ta::kCounterSlabBytes + parts * d * sizeof(float));
+    p.ws_o = reinterpret_cast<float*>(base);
+    p.ws_ml = reinterpret_cast<float*>(base + parts * d * sizeof(float));
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
@@ -197,6 +190,10 @@ int run_attention(const void* q, ta_kv kv, const int32_t* prefix_len, const int3
   } else {
     e = ta::launch_attn_generic(p, dtype, s);
     where = "attention (generic kernel) launch";
+  }
+  if (e == hipSuccess && pl.n_split > 1) {
+    e = ta::launch_attn_merge(p, dtype, s);
+    where = "attention split combine launch";
   }
   return hip_status(e, where);
 }

@@ -12,8 +12,8 @@
 // a split is `chunk` consecutive KV positions.  Each of the 4 waves owns 8
 // rows; a 64-position K/V tile is staged in LDS as fp32, lane j scores
 // position j, and each lane accumulates 2 (d=128) or 1 (d=64) output
-// channels.  Splits merge in the same launch: the last work group to arrive
-// (device-scope counter) combines the partial (max, sum, output) triples.
+// channels.  A split sequence leaves partial (max, sum, output) triples in the
+// workspace for the combine launch (attn_merge.hip).
 #include "ta_device.h"
 
 namespace ta {
@@ -51,7 +51,6 @@ __global__ __launch_bounds__(kThreads) void attn_generic_kernel(AttnParams p) {
   __shared__ uint64_t sAnc[kMaxNodes][kMaskWords];
   __shared__ int sJump[kMaxNodes];
   __shared__ int sNode[kRows];
-  __shared__ int sLast;
 
   const int split = blockIdx.x;
   const int rtile = blockIdx.y;
@@ -200,7 +199,7 @@ __global__ __launch_bounds__(kThreads) void attn_generic_kernel(AttnParams p) {
     return;
   }
 
-  // Publish this split's partial result, then let the last arrival merge.
+  // Publish this split's partial result for the combine launch.
   const int tile_id = bh * p.n_row_tiles + rtile;
   const size_t part = static_cast<size_t>(tile_id) * p.n_split;
 #pragma unroll
@@ -214,44 +213,7 @@ __global__ __launch_bounds__(kThreads) void attn_generic_kernel(AttnParams p) {
       p.ws_ml[((part + split) * kRows + r) * 2 + 1] = l[rr];
     }
   }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const int prev = __hip_atomic_fetch_add(p.ws_cnt + tile_id, 1, __ATOMIC_ACQ_REL,
-                                            __HIP_MEMORY_SCOPE_AGENT);
-    sLast = (prev == nsplit - 1);
-  }
-  __syncthreads();
-  if (!sLast) return;
-  __threadfence();
-
-#pragma unroll
-  for (int rr = 0; rr < 8; ++rr) {
-    const int r = wave * 8 + rr;
-    if (sNode[r] < 0) continue;
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s)
-      M = fmaxf(M, __builtin_nontemporal_load(p.ws_ml + ((part + s) * kRows + r) * 2));
-    float L = 0.f, acc[C];
-#pragma unroll
-    for (int c = 0; c < C; ++c) acc[c] = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float ms = __builtin_nontemporal_load(p.ws_ml + ((part + s) * kRows + r) * 2);
-      const float ls = __builtin_nontemporal_load(p.ws_ml + ((part + s) * kRows + r) * 2 + 1);
-      const float wgt = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
-      L = fmaf(ls, wgt, L);
-      const float* po = p.ws_o + ((part + s) * kRows + r) * D;
-#pragma unroll
-      for (int c = 0; c < C; ++c)
-        acc[c] = fmaf(__builtin_nontemporal_load(po + lane + 64 * c), wgt, acc[c]);
-    }
-    const float inv = 1.f / L;
-#pragma unroll
-    for (int c = 0; c < C; ++c) store_elem<T>(Out, out_index(r, lane + 64 * c), acc[c] * inv);
-    if (p.lse != nullptr && lane == 0) p.lse[lse_index(r)] = (M + log2f(L)) * kLn2;
-  }
-  if (tid == 0)
-    __hip_atomic_store(p.ws_cnt + tile_id, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // the combine launch (attn_merge.hip) finishes split sequences
 }
 
 }  // namespace
@@ -269,8 +231,7 @@ hipError_t launch_attn_generic(const AttnParams& p, int dtype, hipStream_t s) {
 size_t attn_ws_bytes(int tiles, int n_split, int rows_per_tile, int d) {
   if (n_split <= 1) return 0;
   const size_t parts = static_cast<size_t>(tiles) * n_split * rows_per_tile;
-  size_t bytes = kCounterSlabBytes;                // arrival counters, always at offset 0
-  bytes += parts * d * sizeof(float);              // ws_o
+  size_t bytes = parts * d * sizeof(float);        // ws_o
   bytes += parts * 2 * sizeof(float);              // ws_ml
   return bytes;
 }

@@ -1,0 +1,91 @@
+// Split-KV combine (the second launch of a split attention call).
+//
+// Each split s of a (sequence, KV head, row tile) left, per query row, the
+// running maximum m_s (log2 units of the scaled scores), the sum l_s of
+// 2^(score - m_s) and the unnormalised output O_s.  The rows' results are the
+// log-sum-exp combination (SwiftSpec summary, Section 3.3: one head split
+// over several thread blocks, partial results combined):
+//   M = max_s m_s,  L = sum_s 2^(m_s - M) l_s,
+//   O = sum_s 2^(m_s - M) O_s / L,  LSE = (M + log2 L) * ln 2.
+// The combine runs as its own launch: on gfx950 the kernel boundary makes the
+// partial results visible to every compute unit once, whereas a device-scope
+// release/acquire in each splitting work group writes back and invalidates
+// the whole L2 of its XCD every time.
+#include "ta_device.h"
+
+namespace ta {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr float kLn2 = 0.69314718055994530942f;
+
+template <typename T>
+__device__ __forceinline__ void store4(T* out, f32x4 v);
+template <>
+__device__ __forceinline__ void store4<float>(float* out, f32x4 v) {
+  *reinterpret_cast<f32x4*>(out) = v;
+}
+template <>
+__device__ __forceinline__ void store4<uint16_t>(uint16_t* out, f32x4 v) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const uint32_t lo = f32_to_bf16_bits(v[0]) | (static_cast<uint32_t>(f32_to_bf16_bits(v[1])) << 16);
+  const uint32_t hi = f32_to_bf16_bits(v[2]) | (static_cast<uint32_t>(f32_to_bf16_bits(v[3])) << 16);
+  *reinterpret_cast<u32x2*>(out) = u32x2{lo, hi};
+}
+
+// grid = (row-tile x channel-group blocks, sequence x KV head); one thread
+// per (row, 4 channels) of a tile.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void merge_kernel(AttnParams p) {
+  const int bh = blockIdx.y;
+  const int b = bh / p.Hkv;
+  const int hkv = bh % p.Hkv;
+  SeqBounds sb;
+  if (!seq_bounds(p.prefix_len, p.n_nodes, b, p.n_max, p.T_cap, sb)) return;
+  const int nsplit = (sb.T + p.chunk - 1) / p.chunk;
+  if (nsplit <= 1) return;  // the attention kernel wrote this sequence's results
+  const int groups = p.d / 4;
+  const int per_tile = p.rows_per_tile * groups;
+  const int e = blockIdx.x * kThreads + threadIdx.x;
+  const int rtile = e / per_tile;
+  if (rtile >= p.n_row_tiles) return;
+  const int r = (e % per_tile) / groups;
+  const int dg = e % groups;
+  const int gr = rtile * p.rows_per_tile + r;
+  const int R = p.n_q * p.G;
+  if (gr >= R) return;
+  const int slot = gr / p.G, g = gr % p.G;
+  const int node = p.expand ? sb.n - p.n_q + slot : slot;
+  if (node < 0 || node >= sb.n) return;
+
+  const size_t part = static_cast<size_t>(bh * p.n_row_tiles + rtile) * p.n_split;
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s)
+    M = fmaxf(M, p.ws_ml[((part + s) * p.rows_per_tile + r) * 2]);
+  float L = 0.f;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < nsplit; ++s) {
+    const size_t pr = (part + s) * p.rows_per_tile + r;
+    const float ms = p.ws_ml[pr * 2];
+    const float wgt = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
+    L = fmaf(p.ws_ml[pr * 2 + 1], wgt, L);
+    o += *reinterpret_cast<const f32x4*>(p.ws_o + pr * p.d + 4 * dg) * wgt;
+  }
+  const float inv = 1.f / L;
+  T* out = static_cast<T*>(p.out) +
+           ((static_cast<size_t>(b) * p.n_q + slot) * p.Hq + hkv * p.G + g) * p.d + 4 * dg;
+  store4<T>(out, o * inv);
+  if (p.lse != nullptr && dg == 0)
+    p.lse[(static_cast<size_t>(b) * p.Hq + hkv * p.G + g) * p.n_q + slot] = (M + log2f(L)) * kLn2;
+}
+
+}  // namespace
+
+hipError_t launch_attn_merge(const AttnParams& p, int dtype, hipStream_t s) {
+  const long long items = static_cast<long long>(p.n_row_tiles) * p.rows_per_tile * (p.d / 4);
+  const dim3 grid(static_cast<unsigned>((items + kThreads - 1) / kThreads), p.B * p.Hkv);
+  if (dtype == TA_F32) return launch(merge_kernel<float>, grid, dim3(kThreads), s, p);
+  return launch(merge_kernel<uint16_t>, grid, dim3(kThreads), s, p);
+}
+
+}  // namespace ta

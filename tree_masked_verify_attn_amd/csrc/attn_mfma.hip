@@ -30,8 +30,8 @@
 //    (16 consecutive positions, same chunk) and the transposed V reads
 //    (4 positions x 2 chunks) free of bank conflicts.  The next tile is
 //    prefetched into registers while the current one is consumed.
-//  * Splits merge in the same launch: the last work group to arrive (device-
-//    scope counter in the workspace) combines the partial (max, sum, output).
+//  * A split sequence leaves partial (max, sum, output) states in the
+//    workspace; the combine launch (attn_merge.hip) finishes it.
 #include "ta_device.h"
 
 namespace ta {
@@ -86,7 +86,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t sKV[C::LDS_BYTES];
   __shared__ uint64_t sAnc[kMaxNodes][kMaskWords];
   __shared__ int sJump[kMaxNodes];
-  __shared__ int sLast;
   uint8_t* sK = sKV;
   uint8_t* sV = sKV + C::TILE_BYTES;
 
@@ -342,7 +341,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnParams p) {
     return;
   }
 
-  // ---- publish the partial state, the last arrival merges -----------------
+  // ---- publish the partial state for the combine launch --------------------
   const int tile_id = bh * p.n_row_tiles + rtile;
   const size_t part = static_cast<size_t>(tile_id) * p.n_split;
   if (owner) {
@@ -360,52 +359,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnParams p) {
       p.ws_ml[((part + split) * C::RPT + row_in_tile) * 2 + 1] = l_sum;
     }
   }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const int prev = __hip_atomic_fetch_add(p.ws_cnt + tile_id, 1, __ATOMIC_ACQ_REL,
-                                            __HIP_MEMORY_SCOPE_AGENT);
-    sLast = (prev == nsplit - 1);
-  }
-  __syncthreads();
-  if (!sLast) return;
-  __threadfence();
-
-  // Merge: thread (row, 4-channel group) pairs over the tile's rows.
-  constexpr int kGroups = D / 4;
-  for (int e = tid; e < C::RPT * kGroups; e += kThreads) {
-    const int r = e / kGroups, dg = e % kGroups;
-    const int gr = rtile * C::RPT + r;
-    if (gr >= R) continue;
-    const int sl = gr / p.G, gg = gr % p.G;
-    const int nd = p.expand ? sb.n - p.n_q + sl : sl;
-    if (nd < 0 || nd >= sb.n) continue;
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s)
-      M = fmaxf(M, __builtin_nontemporal_load(p.ws_ml + ((part + s) * C::RPT + r) * 2));
-    float L = 0.f;
-    f32x4 o = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < nsplit; ++s) {
-      const float ms = __builtin_nontemporal_load(p.ws_ml + ((part + s) * C::RPT + r) * 2);
-      const float ls = __builtin_nontemporal_load(p.ws_ml + ((part + s) * C::RPT + r) * 2 + 1);
-      const float wgt = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
-      L = fmaf(ls, wgt, L);
-      const f32x4 ps = __builtin_nontemporal_load(
-          reinterpret_cast<const f32x4*>(p.ws_o + ((part + s) * C::RPT + r) * D + 4 * dg));
-      o += ps * wgt;
-    }
-    const float inv = 1.f / L;
-    const size_t orr = ((static_cast<size_t>(b) * p.n_q + sl) * p.Hq + hkv * p.G + gg) * D + 4 * dg;
-    const uint32_t lo = f32_to_bf16_bits(o[0] * inv) |
-                        (static_cast<uint32_t>(f32_to_bf16_bits(o[1] * inv)) << 16);
-    const uint32_t hi = f32_to_bf16_bits(o[2] * inv) |
-                        (static_cast<uint32_t>(f32_to_bf16_bits(o[3] * inv)) << 16);
-    *reinterpret_cast<u32x2*>(Out + orr) = u32x2{lo, hi};
-    if (p.lse != nullptr && dg == 0)
-      p.lse[(static_cast<size_t>(b) * p.Hq + hkv * p.G + gg) * p.n_q + sl] = (M + log2f(L)) * kLn2;
-  }
-  if (tid == 0)
-    __hip_atomic_store(p.ws_cnt + tile_id, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // the combine launch (attn_merge.hip) finishes split sequences
 }
 
 template <int D>

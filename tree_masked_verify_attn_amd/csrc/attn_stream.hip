@@ -17,7 +17,8 @@
 //    consumes every stage; waves beyond the row groups only issue loads.
 //  * Paged caches: the split's block ids are copied to LDS first, so the
 //    ring loop issues no other vector-memory loads.
-//  * Splits merge in the same launch (last arriving work group).
+//  * A split sequence leaves partial (max, sum, output) states in the
+//    workspace; the combine launch (attn_merge.hip) finishes it.
 #include "ta_device.h"
 
 namespace ta {
@@ -105,7 +106,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
   static_assert(S >= 2 && S <= 4, "ring depth");
   __shared__ __attribute__((aligned(1024))) uint8_t sRing[C::LDS];
   __shared__ int sBlk[kMaxSplitBlocks];
-  __shared__ int sLast;
 
   const int split = blockIdx.x;
   const int rtile = blockIdx.y;
@@ -220,36 +220,33 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
   const float cs = p.scale_log2;
   const int lim = min(sb.P, t_end);
 
-  for (int j = 0; j < S - 1 && j < ntiles; ++j) issue_stage(j);
-
-  for (int j = 0; j < ntiles; ++j) {
-    // stage j has landed once at most (stages issued after it) x NL loads are pending
-    wait_stage<S - 2, C::NL>(min(S - 2, ntiles - 1 - j));
-    raw_barrier();  // all waves: stage j visible, stage j-1 no longer read
-    if (j + S - 1 < ntiles) issue_stage(j + S - 1);
-
-    if (rg >= 0) {
+  // One 32-position tile of this wave's rows; `masked` tiles reach the tree
+  // cache or the end of the split, all others take the plain dense path.
+  auto tile = [&](int j, auto masked_tag) {
+    constexpr bool kMasked = decltype(masked_tag)::value;
+    {
       const int tb = t_begin + j * kTile;
       const uint8_t* sK = sRing + (j % S) * C::STAGE;
       const uint8_t* sV = sK + C::HALF;
       f32x16 Sc;
 #pragma unroll
       for (int r = 0; r < 16; ++r) Sc[r] = 0.f;
+      u32x4 ka[C::KS];  // all K operands in flight before the first MFMA
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(sK + lds_off<D>(l32, 2 * ks + lhi));
-        Sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qreg[ks], Sc,
-                                                     0, 0, 0);
-      }
-      if (tb + kTile > lim) {
+      for (int ks = 0; ks < C::KS; ++ks)
+        ka[ks] = *reinterpret_cast<const u32x4*>(sK + lds_off<D>(l32, 2 * ks + lhi));
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks)
+        Sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka[ks]), qreg[ks],
+                                                     Sc, 0, 0, 0);
+      if constexpr (kMasked) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int t = tb + 8 * (r >> 2) + 4 * lhi + (r & 3);
-          bool vis = t < t_end;
-          if (vis && t >= sb.P) {
-            const int jj = t - sb.P;
-            vis = (anc[jj >> 6] >> (jj & 63)) & 1ull;
-          }
+          const int jj = t - sb.P;  // tree column (negative: prefix)
+          const uint64_t word = jj < 64 ? anc[0] : (jj < 128 ? anc[1] : (jj < 192 ? anc[2] : anc[3]));
+          const bool in_tree = ((word >> (jj & 63)) & 1ull) != 0ull;
+          const bool vis = t < t_end && (jj < 0 || in_tree);
           if (!vis) Sc[r] = -INFINITY;
         }
       }
@@ -273,7 +270,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
       bf16x8 pk[2];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float pr = exp2f(fmaf(Sc[r], cs, -m_use));
+        const float pr = __builtin_amdgcn_exp2f(fmaf(Sc[r], cs, -m_use));  // v_exp_f32; args <= 8
         rs += pr;
         pk[r >> 3][r & 7] = static_cast<__bf16>(pr);
       }
@@ -297,6 +294,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
         }
       }
     }
+  };
+  // Ring step j: stage j has landed once at most (stages issued after it) x NL
+  // loads are pending; after the barrier stage j-1 is free for stage j+S-1.
+  auto step = [&](int j) {
+    wait_stage<S - 2, C::NL>(min(S - 2, ntiles - 1 - j));
+    raw_barrier();
+    if (j + S - 1 < ntiles) issue_stage(j + S - 1);
+  };
+
+  for (int j = 0; j < S - 1 && j < ntiles; ++j) issue_stage(j);
+  // tiles entirely below lim = min(P, t_end) need no mask
+  const int n_clean = max(0, min(ntiles, (lim - t_begin) / kTile));
+  for (int j = 0; j < n_clean; ++j) {
+    step(j);
+    if (rg >= 0) tile(j, std::false_type{});
+  }
+  for (int j = n_clean; j < ntiles; ++j) {
+    step(j);
+    if (rg >= 0) tile(j, std::true_type{});
   }
   wait_vmcnt<0>();
   __syncthreads();
@@ -341,51 +357,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
       p.ws_ml[((part + split) * C::RPT + row_in_tile) * 2 + 1] = l_sum;
     }
   }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const int prev = __hip_atomic_fetch_add(p.ws_cnt + tile_id, 1, __ATOMIC_ACQ_REL,
-                                            __HIP_MEMORY_SCOPE_AGENT);
-    sLast = (prev == nsplit - 1);
-  }
-  __syncthreads();
-  if (!sLast) return;
-  __threadfence();
-
-  constexpr int kGroups = D / 4;
-  for (int e = tid; e < C::RPT * kGroups; e += kThreads) {
-    const int r = e / kGroups, dg = e % kGroups;
-    const int gr = rtile * C::RPT + r;
-    if (gr >= R) continue;
-    const int sl = gr / p.G, gg = gr % p.G;
-    const int nd = p.expand ? sb.n - p.n_q + sl : sl;
-    if (nd < 0 || nd >= sb.n) continue;
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s)
-      M = fmaxf(M, __builtin_nontemporal_load(p.ws_ml + ((part + s) * C::RPT + r) * 2));
-    float L = 0.f;
-    f32x4 o = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < nsplit; ++s) {
-      const float ms = __builtin_nontemporal_load(p.ws_ml + ((part + s) * C::RPT + r) * 2);
-      const float ls = __builtin_nontemporal_load(p.ws_ml + ((part + s) * C::RPT + r) * 2 + 1);
-      const float wgt = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
-      L = fmaf(ls, wgt, L);
-      const f32x4 ps = __builtin_nontemporal_load(
-          reinterpret_cast<const f32x4*>(p.ws_o + ((part + s) * C::RPT + r) * D + 4 * dg));
-      o += ps * wgt;
-    }
-    const float inv = 1.f / L;
-    const size_t orr = ((static_cast<size_t>(b) * p.n_q + sl) * p.Hq + hkv * p.G + gg) * D + 4 * dg;
-    const uint32_t lo = f32_to_bf16_bits(o[0] * inv) |
-                        (static_cast<uint32_t>(f32_to_bf16_bits(o[1] * inv)) << 16);
-    const uint32_t hi = f32_to_bf16_bits(o[2] * inv) |
-                        (static_cast<uint32_t>(f32_to_bf16_bits(o[3] * inv)) << 16);
-    *reinterpret_cast<u32x2*>(Out + orr) = u32x2{lo, hi};
-    if (p.lse != nullptr && dg == 0)
-      p.lse[(static_cast<size_t>(b) * p.Hq + hkv * p.G + gg) * p.n_q + sl] = (M + log2f(L)) * kLn2;
-  }
-  if (tid == 0)
-    __hip_atomic_store(p.ws_cnt + tile_id, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // the combine launch (attn_merge.hip) finishes split sequences
 }
 
 template <int D, int S>

@@ -60,18 +60,15 @@ struct AttnParams {
   // workspace (only when n_split > 1)
   float* ws_o;          // [tiles][n_split][rows_per_tile][d] unnormalised partial outputs
   float* ws_ml;         // [tiles][n_split][rows_per_tile][2]  running max (log2) and sum
-  int32_t* ws_cnt;      // [tiles] arrival counters (zero between calls)
 };
 
-// Workspace layout: a fixed slab of arrival counters at offset 0 (so that
-// counters never overlap partial results of a differently sized earlier
-// call), then the partial outputs, then the (max, sum) pairs.
-constexpr size_t kCounterSlabBytes = 64 * 1024;
-constexpr int kMaxTiles = static_cast<int>(kCounterSlabBytes / sizeof(int32_t));
-// Returns the bytes needed for a plan (0 when there is a single split).
+// Workspace layout: the partial outputs, then the (max, sum) pairs.  Returns
+// the bytes needed for a plan (0 when there is a single split).
 size_t attn_ws_bytes(int tiles, int n_split, int rows_per_tile, int d);
 
 hipError_t launch_attn_generic(const AttnParams& p, int dtype, hipStream_t s);
+// Second launch of a split call: combines the partial states into out / lse.
+hipError_t launch_attn_merge(const AttnParams& p, int dtype, hipStream_t s);
 hipError_t launch_attn_mfma(const AttnParams& p, hipStream_t s);
 // Streaming MFMA variant: `stages` (3 or 4) 32-position LDS stages in flight.
 hipError_t launch_attn_stream(const AttnParams& p, int stages, hipStream_t s);
