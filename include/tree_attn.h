@@ -84,7 +84,10 @@ typedef struct {
 /* Optional tuning/testing knobs for the attention calls (NULL = automatic). */
 typedef struct {
   int32_t chunk_tokens;  /* KV tokens per split-KV work item, a multiple of 64; 0 = auto */
-  int32_t kernel;        /* 0 = auto, 1 = generic fp32-math kernel, 2 = bf16 MFMA kernel */
+  int32_t kernel;        /* 0 = auto (3 for bf16, else 1); 1 = generic fp32-math kernel;
+                            2 = bf16 MFMA kernel, register prefetch; 3 = bf16 MFMA kernel,
+                            LDS-DMA ring and pipelined tiles (paged calls whose split spans
+                            more than 510 blocks run on kernel 2) */
 } ta_attn_opts;
 
 /*

@@ -69,7 +69,8 @@ bool make_plan(int B, int n_q, int Hq, int Hkv, int d, int dtype, int T_cap,
   const int R = n_q * G;
   int kernel = opts ? opts->kernel : 0;
   const bool mfma_ok = dtype == TA_BF16 && (d == 128 || d == 64);
-  if (kernel == 0) kernel = mfma_ok ? 2 : 1;
+  // automatic: the streaming MFMA kernel for bf16, the generic kernel otherwise
+  if (kernel == 0) kernel = mfma_ok ? 3 : 1;
   if ((kernel == 2 || kernel == 3) && !mfma_ok) return false;
   if (kernel < 1 || kernel > 3) return false;
   pl.kernel = kernel;

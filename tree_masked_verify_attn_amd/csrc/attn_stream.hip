@@ -100,12 +100,15 @@ __device__ __forceinline__ void wait_stage(int pending_after) {
   wait_vmcnt<0>();
 }
 
+// S = 4: 64 KiB ring, two work groups per compute unit.  S = 3: 48 KiB ring and
+// registers capped for three work groups per compute unit.
 template <int D, int NRG, int S>
-__global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) {
+__global__ __launch_bounds__(kThreads, S == 3 ? 3 : 2) void attn_stream_kernel(AttnParams p) {
   using C = SCfg<D, NRG, S>;
   static_assert(S >= 2 && S <= 4, "ring depth");
   __shared__ __attribute__((aligned(1024))) uint8_t sRing[C::LDS];
   __shared__ int sBlk[kMaxSplitBlocks];
+  __shared__ uint64_t sRowMask[C::RPT][kMaskWords];  // ancestor mask of each row's node
 
   const int split = blockIdx.x;
   const int rtile = blockIdx.y;
@@ -140,7 +143,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
 
   // ---- setup: ancestor masks (in the ring's space), paged block ids ------------
   const bool has_tree = t_end > sb.P;
-  uint64_t anc[kMaskWords] = {0, 0, 0, 0};
   {
     auto sAnc = reinterpret_cast<uint64_t(*)[kMaskWords]>(sRing);
     int* sJump = reinterpret_cast<int*>(sRing + kMaxNodes * kMaskWords * 8);
@@ -154,11 +156,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
       }
     }
     __syncthreads();
-    if (has_tree && node >= 0) {
+    // keep each row's mask (only the tail tile reads it) outside the ring
+    if (has_tree && rg >= 0 && lhi == 0) {
 #pragma unroll
-      for (int w = 0; w < kMaskWords; ++w) anc[w] = sAnc[node][w];
+      for (int w = 0; w < kMaskWords; ++w) sRowMask[row_in_tile][w] = node >= 0 ? sAnc[node][w] : 0ull;
     }
-    __syncthreads();  // the ring may now overwrite the masks
+    __syncthreads();  // the ring may now overwrite the ancestor table
   }
 
   const uint16_t* Q = static_cast<const uint16_t*>(p.q);
@@ -194,16 +197,34 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
     }
     return row * C::ROW;
   };
-  auto issue_stage = [&](int j) {
+  // Per-lane DMA sources: lane (row r, physical chunk pc) of load q fetches
+  // logical chunk pc ^ swz(r).  In the contiguous layout the byte offset of the
+  // next stage to issue just advances by one tile of positions per stage.
+  const bool contiguous = p.block_table == nullptr;
+  const size_t pos_stride = static_cast<size_t>(p.Hkv) * C::ROW;  // contiguous: bytes per position
+  size_t dma_off[C::INST_PER_WAVE];
+#pragma unroll
+  for (int q = 0; q < C::INST_PER_WAVE; ++q) {
+    const int r = (wave * C::INST_PER_WAVE + q) * C::ROWS_PER_INST + lane / C::CH;
+    const int c = (lane % C::CH) ^ swz<D>(r);
+    dma_off[q] = (static_cast<size_t>(b) * p.T_cap + t_begin + r) * pos_stride +
+                 static_cast<size_t>(hkv) * C::ROW + c * 16;
+  }
+  // Issues stage j (the stages are issued in order) into ring slot `slot`.
+  auto issue_stage = [&](int j, int slot) {
     const int tb = t_begin + j * kTile;
-    const uint32_t sbase = ring_base + (j % S) * C::STAGE;
+    const uint32_t sbase = ring_base + slot * C::STAGE;
+    const bool fast = contiguous && tb + kTile <= t_end;
 #pragma unroll
     for (int q = 0; q < C::INST_PER_WAVE; ++q) {
       const int r0 = (wave * C::INST_PER_WAVE + q) * C::ROWS_PER_INST;
-      const int r = r0 + lane / C::CH;
-      const int pc = lane % C::CH;
-      const int c = pc ^ swz<D>(r);
-      const size_t off = row_bytes_off(tb + r) + c * 16;
+      size_t off = dma_off[q];
+      if (!fast) {
+        const int r = r0 + lane / C::CH;
+        const int c = (lane % C::CH) ^ swz<D>(r);
+        off = row_bytes_off(tb + r) + c * 16;
+      }
+      dma_off[q] += kTile * pos_stride;
       const uint32_t lk = __builtin_amdgcn_readfirstlane(sbase + r0 * C::ROW);
       dma16(Kg + off, lk);
       dma16(Vg + off, lk + C::HALF);
@@ -220,99 +241,142 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
   const float cs = p.scale_log2;
   const int lim = min(sb.P, t_end);
 
-  // One 32-position tile of this wave's rows; `masked` tiles reach the tree
-  // cache or the end of the split, all others take the plain dense path.
-  auto tile = [&](int j, auto masked_tag) {
+  // S^T = K . Q^T for the tile in ring `slot` (M = 32 positions, N = 32 rows,
+  // K = d).  The MFMAs run while the previous tile's softmax uses the VALU.
+  auto qk = [&](int slot) -> f32x16 {
+    const uint8_t* sK = sRing + slot * C::STAGE;
+    f32x16 Sc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Sc[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(sK + lds_off<D>(l32, 2 * ks + lhi));
+      Sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qreg[ks], Sc,
+                                                   0, 0, 0);
+    }
+    return Sc;
+  };
+  // Per-lane bases of the transposed V reads: lane (group gi, index jl) reads
+  // positions 16kk + 8h + 4(gi/2) + jl/4 at channels 32mb + 16(gi%2) + 4(jl%4);
+  // under the swizzle that is base +- 64 x + (16kk + 8h) ROW + 64 (mb ^ 2h).
+  int v_base_p, v_base_m;
+  {
+    const int gi = lane >> 4, jl = lane & 15;
+    const int x = (jl >> 3) & 1;
+    const int s_lo = (((jl >> 2) & 1) << 1) | ((gi >> 1) & 1);
+    const int y = (2 * (gi & 1) + ((jl & 3) >> 1)) ^ s_lo;
+    const int L = (4 * (gi >> 1) + (jl >> 2)) * C::ROW + 16 * y + 8 * (jl & 1);
+    v_base_p = L + 64 * x;
+    v_base_m = L - 64 * x;
+  }
+  // Mask (tiles that reach the tree cache or the split's end), online softmax
+  // and O^T += V^T . P^T for tile j held in ring `slot`.  Lane l holds
+  // positions tb + 8*(r/4) + 4*lhi + r%4 of row l32.
+  auto softmax_pv = [&](f32x16 Sc, int j, int slot, auto masked_tag) {
     constexpr bool kMasked = decltype(masked_tag)::value;
-    {
-      const int tb = t_begin + j * kTile;
-      const uint8_t* sK = sRing + (j % S) * C::STAGE;
-      const uint8_t* sV = sK + C::HALF;
-      f32x16 Sc;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) Sc[r] = 0.f;
-      u32x4 ka[C::KS];  // all K operands in flight before the first MFMA
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks)
-        ka[ks] = *reinterpret_cast<const u32x4*>(sK + lds_off<D>(l32, 2 * ks + lhi));
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks)
-        Sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka[ks]), qreg[ks],
-                                                     Sc, 0, 0, 0);
-      if constexpr (kMasked) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int t = tb + 8 * (r >> 2) + 4 * lhi + (r & 3);
-          const int jj = t - sb.P;  // tree column (negative: prefix)
-          const uint64_t word = jj < 64 ? anc[0] : (jj < 128 ? anc[1] : (jj < 192 ? anc[2] : anc[3]));
-          const bool in_tree = ((word >> (jj & 63)) & 1ull) != 0ull;
-          const bool vis = t < t_end && (jj < 0 || in_tree);
-          if (!vis) Sc[r] = -INFINITY;
-        }
-      }
-      float mx = Sc[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, Sc[r]);
-      mx = fmaxf(mx, lane_swap32(mx)) * cs;
-      const bool bump = mx > m_ref + kRescaleSlack;
-      if (__builtin_amdgcn_ballot_w64(bump) != 0ull) {
-        const float m_new = bump ? mx : m_ref;
-        const float alpha = (m_ref == -INFINITY) ? 0.f : exp2f(m_ref - m_new);
-        l_sum *= alpha;
-#pragma unroll
-        for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[mb][r] *= alpha;
-        m_ref = m_new;
-      }
-      const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-      float rs = 0.f;
-      bf16x8 pk[2];
+    const int tb = t_begin + j * kTile;
+    const uint8_t* sV = sRing + slot * C::STAGE + C::HALF;
+    if constexpr (kMasked) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float pr = __builtin_amdgcn_exp2f(fmaf(Sc[r], cs, -m_use));  // v_exp_f32; args <= 8
-        rs += pr;
-        pk[r >> 3][r & 7] = static_cast<__bf16>(pr);
+        const int t = tb + 8 * (r >> 2) + 4 * lhi + (r & 3);
+        const int jj = t - sb.P;  // tree column (negative: prefix)
+        const bool tree_col = jj >= 0 && t < t_end;  // then jj < n <= 256
+        const uint64_t word = tree_col ? sRowMask[row_in_tile][jj >> 6] : 0ull;
+        const bool in_tree = ((word >> (jj & 63)) & 1ull) != 0ull;
+        const bool vis = t < t_end && (jj < 0 || in_tree);
+        if (!vis) Sc[r] = -INFINITY;
       }
-      l_sum += rs + lane_swap32(rs);
+    }
+    float mx = Sc[0];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, Sc[r]);
+    mx = fmaxf(mx, lane_swap32(mx)) * cs;
+    const bool bump = mx > m_ref + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(bump) != 0ull) {
+      const float m_new = bump ? mx : m_ref;
+      const float alpha = (m_ref == -INFINITY) ? 0.f : exp2f(m_ref - m_new);
+      l_sum *= alpha;
 #pragma unroll
-        for (int mb = 0; mb < C::MB; ++mb) {
-          const int gi = lane >> 4, jl = lane & 15;
-          const int d0 = 32 * mb + 16 * (gi & 1);
-          const int trow = 16 * kk + 4 * (gi >> 1) + (jl >> 2);
-          const int dd = d0 + 4 * (jl & 3);
-          const int o1 = lds_off<D>(trow, dd >> 3) + (dd & 7) * 2;
-          const int o2 = lds_off<D>(trow + 8, dd >> 3) + (dd & 7) * 2;
-          const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sV + o1));
-          const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sV + o2));
-          const u32x2 w1 = __builtin_bit_cast(u32x2, v1), w2 = __builtin_bit_cast(u32x2, v2);
-          const u32x4 w = {w1[0], w1[1], w2[0], w2[1]};
-          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pk[kk],
-                                                            acc[mb], 0, 0, 0);
-        }
+      for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mb][r] *= alpha;
+      m_ref = m_new;
+    }
+    const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+    float rs = 0.f;
+    bf16x8 pk[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float pr = __builtin_amdgcn_exp2f(fmaf(Sc[r], cs, -m_use));  // v_exp_f32; args <= 8
+      rs += pr;
+      pk[r >> 3][r & 7] = static_cast<__bf16>(pr);
+    }
+    l_sum += rs + lane_swap32(rs);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb) {
+        // 16-lane group: 4 positions x 16 channels, transposed on read.  With
+        // the swizzle, every address is one of two per-lane bases (by parity of
+        // the swizzled channel block) plus a constant.
+        const int m1 = mb, m2 = mb ^ (D == 128 ? 2 : 0);
+        const int o1 = ((m1 & 1) ? v_base_m : v_base_p) + (16 * kk) * C::ROW + 64 * m1;
+        const int o2 = ((m2 & 1) ? v_base_m : v_base_p) + (16 * kk + 8) * C::ROW + 64 * m2;
+        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sV + o1));
+        const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sV + o2));
+        const u32x2 w1 = __builtin_bit_cast(u32x2, v1), w2 = __builtin_bit_cast(u32x2, v2);
+        const u32x4 w = {w1[0], w1[1], w2[0], w2[1]};
+        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pk[kk],
+                                                          acc[mb], 0, 0, 0);
       }
     }
   };
-  // Ring step j: stage j has landed once at most (stages issued after it) x NL
-  // loads are pending; after the barrier stage j-1 is free for stage j+S-1.
-  auto step = [&](int j) {
-    wait_stage<S - 2, C::NL>(min(S - 2, ntiles - 1 - j));
+  // Makes tile j visible to every wave: wait until stage j has landed (at most
+  // (stages issued after it) x NL loads of this wave pending), then barrier.
+  // After the barrier no wave still reads the slot of tile j-2, which then
+  // receives stage j+S-2.
+  auto arrive = [&](int j, int slot) {
+    // stages issued so far: 0 .. S-2 by the prologue, then t+S-2 by arrive(t), t = 1 .. j-1
+    const int issued_last = min(j == 0 ? S - 2 : j + S - 3, ntiles - 1);
+    wait_stage<S - 2, C::NL>(issued_last - j);
     raw_barrier();
-    if (j + S - 1 < ntiles) issue_stage(j + S - 1);
+    if (j >= 1 && j + S - 2 < ntiles) issue_stage(j + S - 2, (slot + S - 2) % S);
   };
 
-  for (int j = 0; j < S - 1 && j < ntiles; ++j) issue_stage(j);
-  // tiles entirely below lim = min(P, t_end) need no mask
+  // Prologue: stages 0 .. S-2 in flight, tile 0's scores started.
+  for (int j = 0; j < S - 1 && j < ntiles; ++j) issue_stage(j, j);
+  arrive(0, 0);
+  f32x16 s_cur = rg >= 0 ? qk(0) : f32x16{};
+  // Iteration j: tile j+1 arrives and its scores start on the matrix cores,
+  // then tile j's softmax and P.V run.  Tiles below lim = min(P, t_end) need no
+  // mask; the dense part is unrolled by the ring depth so that every slot
+  // offset is a constant.
   const int n_clean = max(0, min(ntiles, (lim - t_begin) / kTile));
-  for (int j = 0; j < n_clean; ++j) {
-    step(j);
-    if (rg >= 0) tile(j, std::false_type{});
+  int j = 0;
+  for (; j + S <= n_clean && j + S < ntiles; j += S) {
+#pragma unroll
+    for (int u = 0; u < S; ++u) {
+      arrive(j + u + 1, (u + 1) % S);
+      if (rg >= 0) {
+        const f32x16 s_next = qk((u + 1) % S);
+        softmax_pv(s_cur, j + u, u, std::false_type{});
+        s_cur = s_next;
+      }
+    }
   }
-  for (int j = n_clean; j < ntiles; ++j) {
-    step(j);
-    if (rg >= 0) tile(j, std::true_type{});
+  for (; j < ntiles; ++j) {
+    const bool more = j + 1 < ntiles;
+    if (more) arrive(j + 1, (j + 1) % S);
+    if (rg >= 0) {
+      f32x16 s_next = {};
+      if (more) s_next = qk((j + 1) % S);
+      if (j < n_clean)
+        softmax_pv(s_cur, j, j % S, std::false_type{});
+      else
+        softmax_pv(s_cur, j, j % S, std::true_type{});
+      s_cur = s_next;
+    }
   }
   wait_vmcnt<0>();
   __syncthreads();
