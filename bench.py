@@ -251,7 +251,8 @@ def main(argv=None):
     traffic = read_traffic()
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": traffic, "kernel": "tree_attn_verify (one launch)",
+                "traffic": traffic,
+                "kernel": "tree_attn_verify call = attention kernel + split-combine kernel",
                 "algorithmic_bytes_per_launch": alg["total"],
                 "avg_launch_us": round(v_avg_s * 1e6, 2)}
 
