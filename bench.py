@@ -1,25 +1,46 @@
 """Benchmark of the tree-verify hot path on one MI355X.
 
-One step = one pass of the whole path over one batch of the chain-verify
-workload (batch 16, Hq=64, Hkv=8, d=128, bf16, prefix 32768 per sequence,
-D = 15 chain drafts -> 128 query rows per KV head):
+Default workload, ``chain_verify``: batch 16, Hq=64, Hkv=8, d=128, bf16,
+prefix 32768 per sequence, D = 15 chain drafts -> 128 query rows per KV head.
+One step = one pass of the whole path over one batch:
 
     tree_attn_verify -> accept_greedy_path -> tree_cache_reroot
 
 followed by restoring the three tiny per-sequence arrays the re-root rewrote
-(prefix_len, parent, n_nodes), so that every step sees the same input.  All
-inputs are resident in HBM before timing starts.  The KV cache is 2.15 GB per
-call, far beyond the 256 MB Infinity Cache, so every step reads it cold.
+(prefix_len, parent, n_nodes: one small elementwise kernel), so that every
+step sees the same input.  All inputs are resident in HBM before timing
+starts.  The KV cache is 2.15 GB per call, far beyond the 256 MB Infinity
+Cache, so every step reads it cold.
+
+By default the K timed steps are captured once in a HIP graph and replayed
+(the entry points read every size from device memory and allocate nothing, so
+a decode loop can do the same); ``--eager`` issues every call from Python
+inside the timed region instead.
+
+Other workloads (``--workload``), each printing the same kind of line:
+
+  paged_alternating  two batches of 32 requests, prefix ~ U[512, 8192], paged
+                     KV in 16-token blocks, chain k = 5, Hq=64, Hkv=8, d=128;
+                     step s runs the path on batch s mod 2 while the other
+                     batch's blocks stay resident (1.14 GB of KV in all).
+  tree_verify_l70b   batch 8, Hq=16, Hkv=2, d=128, prefix 4096, 8-node random
+                     trees; step s reads KV copy s mod 16 (16 layers' worth,
+                     538 MB), so no step finds its KV in the Infinity Cache.
+  draft_expand       batch 1, Hq=32, Hkv=8, d=128, prefix 2048, a 64-node tree
+                     grown by 4 rounds of 8 new leaves (seeded random parents);
+                     one step = the 4 tree_attn_expand calls, on KV copy
+                     s mod 64 (563 MB in all).
 
 Prints one JSON line (metric, value = microseconds per step, roofline of the
-verify kernel, CPU-oracle baseline on a bounded sample).
+attention call, CPU-oracle baseline on a bounded sample).
 
-    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--workload W] [--steps K] [--warmup W] [--eager] [--no-cpu-baseline]
     python bench.py --copy-calib     # plain device copy of known size (PMC scaling)
 """
 from __future__ import annotations
 
 import argparse
+import copy
 import hashlib
 import json
 import os
@@ -32,11 +53,16 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD's published peak
 METRIC = "tree-verify attention µs/step + achieved KV-read GB/s (% of MI355X HBM peak)"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "verify_attn_chain_verify_traffic.txt")
+WORKLOADS = ("chain_verify", "paged_alternating", "tree_verify_l70b", "draft_expand")
+PHASE_REPS = 5                  # timed replays of each single-phase graph
 
 
 def _log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"verify_attn_{workload}_traffic.txt")
 
 
 def kernel_source_hash() -> str:
@@ -49,13 +75,14 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic():
-    """HBM bytes per verify launch from the committed PMC summary, if it still
+def read_traffic(workload: str):
+    """HBM bytes per attention call from the committed PMC summary, if it still
     describes the current kernel sources; else None."""
-    if not os.path.exists(TRAFFIC_FILE):
+    path = traffic_file(workload)
+    if not os.path.exists(path):
         return None
     kv = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if "=" in line and not line.lstrip().startswith("#"):
             a, b = line.split("=", 1)
             kv[a.strip()] = b.strip()
@@ -67,59 +94,321 @@ def read_traffic():
         return None
 
 
-def algorithmic_bytes(c) -> dict:
-    """Bytes the method must move per verify call: K and V once per (sequence,
-    KV head) over P + n positions, Q in, O out, LSE out."""
-    eb = 2 if c.dtype == "bf16" else 4
-    kv = 0
-    for b in range(c.B):
-        T = int(c.prefix_len[b] + c.n_nodes[b])
-        kv += 2 * T * c.Hkv * c.d * eb
-    rows = int(c.n_nodes.sum())
-    q = rows * c.Hq * c.d * eb
-    return {"kv": kv, "q": q, "o": q, "lse": rows * c.Hq * 4,
-            "total": kv + 2 * q + rows * c.Hq * 4}
+def attn_bytes(prefix_len, n_nodes, n_rows, Hq, Hkv, d, eb=2) -> dict:
+    """Bytes an attention call must move: K and V once per (sequence, KV head)
+    over P + n positions, Q in, O out, LSE out (n_rows query rows per sequence)."""
+    kv = sum(2 * (int(p) + int(n)) * Hkv * d * eb for p, n in zip(prefix_len, n_nodes))
+    rows = sum(int(r) for r in n_rows)
+    q = rows * Hq * d * eb
+    return {"kv": kv, "q": q, "o": q, "lse": rows * Hq * 4, "total": kv + 2 * q + rows * Hq * 4}
 
 
-def cpu_baseline(c, budget_s: float = 12.0) -> dict:
-    """Time the oracle (as it stands) on a bounded sample of the same step and
-    scale to microseconds per full step."""
+def _blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        return 1
+
+
+def _subcase(c, sl):
+    """The requests ``sl`` of a case, as a case of their own (host arrays only)."""
+    s = copy.copy(c)
+    for name in ("q", "prefix_len", "parent", "n_nodes", "tok", "root_tok", "logits",
+                 "block_table"):
+        val = getattr(c, name)
+        if val is not None:
+            setattr(s, name, val[sl])
+    if c.block_table is None:
+        s.k, s.v = c.k[sl], c.v[sl]
+    s.B = s.q.shape[0]
+    return s
+
+
+def cpu_verify_step(c, budget_s: float) -> dict:
+    """Time the oracle (as it stands) on a bounded sample of one verify step of
+    case ``c`` (attention blocks, then accept and re-root) and scale it to
+    microseconds per full step."""
     import numpy as np
 
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        blas = 1
     pairs = [(b, hk) for b in range(c.B) for hk in range(c.Hkv)]
-    rng = np.random.default_rng(0)
-    order = rng.permutation(len(pairs))
+    order = np.random.default_rng(0).permutation(len(pairs))
     t_attn, done = 0.0, 0
     for j in order:
         b, hk = pairs[j]
-        heads = list(range(hk * c.G, (hk + 1) * c.G))
         t0 = time.perf_counter()
-        oracle.verify(c, batches=[b], heads=heads)
+        oracle.verify(c, batches=[b], heads=list(range(hk * c.G, (hk + 1) * c.G)))
         t_attn += time.perf_counter() - t0
         done += 1
         if t_attn >= budget_s:
             break
-    t0 = time.perf_counter()
     nb = min(4, c.B)
-    pr, lr, br = oracle.accept_greedy_path(c.logits[:nb], c.parent[:nb], c.tok[:nb],
-                                           c.n_nodes[:nb], c.root_tok[:nb])
+    t0 = time.perf_counter()
+    pr, lr, _ = oracle.accept_greedy_path(c.logits[:nb], c.parent[:nb], c.tok[:nb],
+                                          c.n_nodes[:nb], c.root_tok[:nb])
     t_acc = time.perf_counter() - t0
     t0 = time.perf_counter()
     oracle.tree_cache_reroot([], c.prefix_len[:nb], c.parent[:nb], c.n_nodes[:nb], pr, lr,
                              np.zeros(nb, dtype=bool))
     t_rr = time.perf_counter() - t0
     per_step = t_attn / done * len(pairs) + (t_acc + t_rr) / nb * c.B
-    return {"value": per_step * 1e6, "unit": "us/step", "cores": int(blas), "kind": "oracle",
+    return {"value": per_step * 1e6, "unit": "us/step", "cores": _blas_threads(), "kind": "oracle",
             "sample": f"{done} of {len(pairs)} (sequence, KV head) attention blocks "
                       f"({t_attn:.1f} s) + accept/re-root of {nb} of {c.B} sequences, "
                       f"scaled to one full step",
             "host_cpus": len(os.sched_getaffinity(0))}
+
+
+# ----------------------------------------------------------------------------
+# workloads: each builds device inputs once and exposes step(i, marks)
+# ----------------------------------------------------------------------------
+
+class _Up:
+    def __init__(self, dev):
+        self.dev = dev
+
+    def __call__(self, arr, bf16=False):
+        import numpy as np
+        import torch
+        t = torch.from_numpy(np.ascontiguousarray(arr.view(np.int16) if bf16 else arr)).to(self.dev)
+        return t.view(torch.bfloat16) if bf16 else t
+
+
+class _VerifyBatch:
+    """Device arrays of one verify batch: attention, accept and re-root."""
+
+    def __init__(self, ta, up, c, kv, q):
+        import numpy as np
+        import torch
+        dev = up.dev
+        self.ta, self.torch, self.c, self.kv, self.q = ta, torch, c, kv, q
+        # prefix_len, parent and n_nodes share one buffer so that a single
+        # kernel restores all three after the re-root has rewritten them
+        B, nm = c.B, c.n_max
+        i32 = lambda x: up(np.ascontiguousarray(x, dtype=np.int32)).view(-1)  # noqa: E731
+        self.meta0 = torch.cat([i32(c.prefix_len), i32(c.parent), i32(c.n_nodes)])
+        self.meta = self.meta0.clone()
+        self.P = self.meta[:B]
+        self.par = self.meta[B:B + B * nm].view(B, nm)
+        self.n = self.meta[B + B * nm:]
+        self.tok, self.root_tok, self.logits = up(c.tok), up(c.root_tok), up(c.logits)
+        self.keep = torch.zeros(c.B, dtype=torch.uint8, device=dev)
+        self.out = torch.empty_like(q)
+        self.lse = torch.empty((c.B, c.Hq, c.n_max), dtype=torch.float32, device=dev)
+        self.path = torch.empty((c.B, c.n_max), dtype=torch.int32, device=dev)
+        self.plen = torch.empty((c.B,), dtype=torch.int32, device=dev)
+        self.bonus = torch.empty((c.B,), dtype=torch.int32, device=dev)
+        self.bytes = attn_bytes(c.prefix_len, c.n_nodes, c.n_nodes, c.Hq, c.Hkv, c.d)
+
+    def phase(self, j, ws, opts, kv=None, q=None, logits=None):
+        """Phase j of one step: 0 verify attention, 1 accept, 2 re-root + restore."""
+        ta = self.ta
+        kv = self.kv if kv is None else kv
+        if j == 0:
+            ta.tree_attn_verify(self.q if q is None else q, kv, self.P, self.par, self.n,
+                                self.c.scale, out=self.out, lse=self.lse, workspace=ws, **opts)
+        elif j == 1:
+            ta.accept_greedy_path(self.logits if logits is None else logits, self.par, self.tok,
+                                  self.n, self.root_tok, self.path, self.plen, self.bonus)
+        else:
+            ta.tree_cache_reroot([kv], self.P, self.par, self.n, self.path, self.plen, self.keep)
+            # an elementwise kernel, not a device copy, so that it graph-captures
+            # as a kernel node
+            torch = self.torch
+            torch.add(self.meta0, 0, out=self.meta)
+
+
+class _Workload:
+    def step(self, i, ws, marks, opts):
+        for j in range(len(self.phases)):
+            if marks is not None:
+                marks[j].record()
+            self.phase(i, j, ws, opts)
+        if marks is not None:
+            marks[len(self.phases)].record()
+
+
+class ChainVerify(_Workload):
+    phases = ("verify", "accept", "reroot")
+
+    def __init__(self, ta, up):
+        from gen import config2_chain
+        c = self.c = config2_chain()
+        self.batch = _VerifyBatch(ta, up, c, ta.KVCache(up(c.k, True), up(c.v, True)),
+                                  up(c.q, True))
+        self.config = {"workload": "chain_verify", "batch": c.B, "Hq": c.Hq, "Hkv": c.Hkv,
+                       "head_dim": c.d, "prefix": int(c.prefix_len[0]), "D": c.n_max - 1,
+                       "rows_per_kv_head": c.G * c.n_max, "vocab": c.vocab,
+                       "step": "verify + accept + re-root (+ restore of 3 tiny arrays)"}
+
+    def phase(self, i, j, ws, opts):
+        self.batch.phase(j, ws, opts)
+
+    def attn_bytes(self, i):
+        return self.batch.bytes
+
+    def check(self):
+        if self.batch.plen.cpu().tolist() != self.c.planted["path_len"]:
+            raise RuntimeError("accepted lengths differ from the planted ones")
+
+    def cpu_baseline(self, budget):
+        return cpu_verify_step(self.c, budget)
+
+
+class PagedAlternating(_Workload):
+    phases = ("verify", "accept", "reroot")
+
+    def __init__(self, ta, up):
+        from gen import config5_paged
+        c = self.c = config5_paged()
+        m = self.m = c.planted["batch_size"]
+        k, v = up(c.k, True), up(c.v, True)
+        self.batches = []
+        for s in range(2):
+            sub = _subcase(c, slice(s * m, (s + 1) * m))
+            kv = ta.KVCache(k, v, up(sub.block_table), T_cap=c.T_cap)
+            self.batches.append(_VerifyBatch(ta, up, sub, kv, up(sub.q, True)))
+        self.config = {"workload": "paged_alternating", "batch": m, "resident_requests": c.B,
+                       "Hq": c.Hq, "Hkv": c.Hkv, "head_dim": c.d, "prefix": "U[512,8192]",
+                       "block_size": c.block_size, "k": c.n_max - 1, "vocab": c.vocab,
+                       "step": "verify + accept + re-root of batch (step mod 2)"}
+
+    def phase(self, i, j, ws, opts):
+        self.batches[i % 2].phase(j, ws, opts)
+
+    def attn_bytes(self, i):
+        return self.batches[i % 2].bytes
+
+    def check(self):
+        for s, bt in enumerate(self.batches):
+            want = self.c.planted["path_len"][s * self.m:(s + 1) * self.m]
+            if bt.plen.cpu().tolist() != want:
+                raise RuntimeError(f"batch {s}: accepted lengths differ from the planted ones")
+
+    def cpu_baseline(self, budget):
+        return cpu_verify_step(self.batches[0].c, budget)
+
+
+class TreeVerifyL70b(_Workload):
+    """Rotates over COPIES sets of (K, V, Q, logits) so that nothing a step
+    reads is left in the Infinity Cache by the previous steps."""
+    phases = ("verify", "accept", "reroot")
+    COPIES = 16
+
+    def __init__(self, ta, up):
+        from gen import config3_tree
+        c = self.c = config3_tree()
+        k, v, q, lg = up(c.k, True), up(c.v, True), up(c.q, True), up(c.logits)
+        self.kvs = [ta.KVCache(k.clone(), v.clone()) for _ in range(self.COPIES)]
+        self.qs = [q.clone() for _ in range(self.COPIES)]
+        self.lgs = [lg.clone() for _ in range(self.COPIES)]
+        del k, v, q, lg
+        self.batch = _VerifyBatch(ta, up, c, self.kvs[0], self.qs[0])
+        self.config = {"workload": "tree_verify_l70b", "batch": c.B, "Hq": c.Hq, "Hkv": c.Hkv,
+                       "head_dim": c.d, "prefix": int(c.prefix_len[0]), "tree_nodes": c.n_max,
+                       "vocab": c.vocab, "kv_copies": self.COPIES,
+                       "step": "verify + accept + re-root (+ restore of 3 tiny arrays)"}
+
+    def phase(self, i, j, ws, opts):
+        c = i % self.COPIES
+        self.batch.phase(j, ws, opts, kv=self.kvs[c], q=self.qs[c], logits=self.lgs[c])
+
+    def attn_bytes(self, i):
+        return self.batch.bytes
+
+    def check(self):
+        if self.batch.plen.cpu().tolist() != self.c.planted["path_len"]:
+            raise RuntimeError("accepted lengths differ from the planted ones")
+
+    def cpu_baseline(self, budget):
+        return cpu_verify_step(self.c, budget)
+
+
+class DraftExpand(_Workload):
+    """Four expansion rounds of w = 8 leaves over a 64-node tree.  Which
+    existing node each new leaf hangs under is drawn at random (seeded): the
+    attention cost does not depend on it, and choosing leaves is not part of
+    the timed path."""
+    phases = ("expand",)
+    COPIES = 64
+
+    def __init__(self, ta, up):
+        import numpy as np
+        import torch
+        from gen import config4_expand
+        e = self.e = config4_expand()
+        self.ta = ta
+        k, v = up(e.k, True), up(e.v, True)
+        self.kvs = [ta.KVCache(k.clone(), v.clone()) for _ in range(self.COPIES)]
+        del k, v
+        rng = np.random.default_rng([4, 999])
+        par = np.full((1, e.n_max), -1, dtype=np.int32)
+        par[0, : e.n0] = e.parent0
+        self.rounds = []
+        n = e.n0
+        for r in range(e.rounds):
+            par[0, n: n + e.w] = rng.integers(0, n, size=e.w)
+            n += e.w
+            self.rounds.append((up(par.copy()), up(np.array([n], np.int32)),
+                                up(e.q_new[r], True)))
+        self.P = up(np.array([e.P], np.int32))
+        self.outs = [torch.empty_like(q) for _, _, q in self.rounds]
+        self.lses = [torch.empty((1, e.Hq, e.w), dtype=torch.float32, device=up.dev)
+                     for _ in self.rounds]
+        b = [attn_bytes([e.P], [e.n0 + e.w * (r + 1)], [e.w], e.Hq, e.Hkv, e.d)
+             for r in range(e.rounds)]
+        self.bytes = {key: sum(x[key] for x in b) for key in b[0]}
+        self.config = {"workload": "draft_expand", "batch": 1, "Hq": e.Hq, "Hkv": e.Hkv,
+                       "head_dim": e.d, "prefix": e.P, "tree_nodes": f"{e.n0}->{e.n_max}",
+                       "w": e.w, "rounds": e.rounds, "kv_copies": self.COPIES,
+                       "step": "4 expansion attention calls (one per round)"}
+
+    def phase(self, i, j, ws, opts):
+        kv = self.kvs[i % self.COPIES]
+        for r, (par, n, q) in enumerate(self.rounds):
+            self.ta.tree_attn_expand(q, kv, self.P, par, n, self.e.scale, out=self.outs[r],
+                                     lse=self.lses[r], workspace=ws, **opts)
+
+    def attn_bytes(self, i):
+        return self.bytes
+
+    def check(self):
+        import torch
+        for o, l in zip(self.outs, self.lses):
+            if not (torch.isfinite(o.float()).all() and torch.isfinite(l).all()):
+                raise RuntimeError("non-finite expansion output")
+
+    def cpu_baseline(self, budget):
+        import numpy as np
+
+        import oracle
+        e = self.e
+        t0 = time.perf_counter()
+        for r, (par, n, _) in enumerate(self.rounds):
+            oc = copy.copy(self.c_like())
+            oc.parent = par.cpu().numpy()
+            oc.n_nodes = n.cpu().numpy()
+            oracle.expand(oc, e.q_new[r], e.w)
+        dt = time.perf_counter() - t0
+        return {"value": dt * 1e6, "unit": "us/step", "cores": _blas_threads(), "kind": "oracle",
+                "sample": "all 4 expansion rounds of one step (no sampling)",
+                "host_cpus": len(os.sched_getaffinity(0))}
+
+    def c_like(self):
+        import numpy as np
+
+        class _C:
+            pass
+        e, oc = self.e, _C()
+        oc.B, oc.Hq, oc.d, oc.G, oc.scale, oc.dtype = 1, e.Hq, e.d, e.Hq // e.Hkv, e.scale, "bf16"
+        oc.prefix_len = np.array([e.P])
+        oc.k, oc.v, oc.block_table, oc.block_size = e.k, e.v, None, 0
+        return oc
+
+
+RUNNERS = {"chain_verify": ChainVerify, "paged_alternating": PagedAlternating,
+           "tree_verify_l70b": TreeVerifyL70b, "draft_expand": DraftExpand}
 
 
 def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
@@ -145,6 +434,7 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", choices=WORKLOADS, default="chain_verify")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--copy-calib", action="store_true",
@@ -152,6 +442,8 @@ def main(argv=None):
     ap.add_argument("--kernel", type=int, default=0,
                     help="0 auto, 1 generic, 2 MFMA (register prefetch), 3 MFMA (LDS-DMA ring)")
     ap.add_argument("--chunk", type=int, default=0, help="KV positions per split (0 = auto)")
+    ap.add_argument("--eager", action="store_true",
+                    help="issue every call from Python inside the timed region (no HIP graph)")
     a = ap.parse_args(argv)
 
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -164,7 +456,6 @@ def main(argv=None):
     import torch
 
     import tree_masked_verify_attn_amd as ta
-    from gen import config2_chain
     from tree_masked_verify_attn_amd import build as tb
 
     if not torch.cuda.is_available():
@@ -182,79 +473,86 @@ def main(argv=None):
 
     dev = torch.device("cuda:0")
     t0 = time.time()
-    c = config2_chain()
-    _log(f"generated chain-verify inputs in {time.time() - t0:.1f} s")
-
-    def up(arr, bf16=False):
-        t = torch.from_numpy(np.ascontiguousarray(arr.view(np.int16) if bf16 else arr)).to(dev)
-        return t.view(torch.bfloat16) if bf16 else t
-
-    q, k, v = up(c.q, True), up(c.k, True), up(c.v, True)
-    P0, par0, n0 = up(c.prefix_len), up(c.parent), up(c.n_nodes)
-    P, par, n = P0.clone(), par0.clone(), n0.clone()
-    tok, root_tok, logits = up(c.tok), up(c.root_tok), up(c.logits)
-    keep = torch.zeros(c.B, dtype=torch.uint8, device=dev)
-    kv = ta.KVCache(k, v)
-    out = torch.empty_like(q)
-    lse = torch.empty((c.B, c.Hq, c.n_max), dtype=torch.float32, device=dev)
-    path = torch.empty((c.B, c.n_max), dtype=torch.int32, device=dev)
-    plen = torch.empty((c.B,), dtype=torch.int32, device=dev)
-    bonus = torch.empty((c.B,), dtype=torch.int32, device=dev)
+    w = RUNNERS[a.workload](ta, _Up(dev))
+    _log(f"generated {a.workload} inputs in {time.time() - t0:.1f} s")
     ws = ta.Workspace(dev)
+    opts = {"kernel": a.kernel, "chunk_tokens": a.chunk}
     torch.cuda.synchronize()
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-
-    def step(marks=None):
-        if marks is not None:
-            marks[0].record()
-        ta.tree_attn_verify(q, kv, P, par, n, c.scale, out=out, lse=lse, workspace=ws,
-                            kernel=a.kernel, chunk_tokens=a.chunk)
-        if marks is not None:
-            marks[1].record()
-        ta.accept_greedy_path(logits, par, tok, n, root_tok, path, plen, bonus)
-        if marks is not None:
-            marks[2].record()
-        ta.tree_cache_reroot([kv], P, par, n, path, plen, keep)
-        if marks is not None:
-            marks[3].record()
-        P.copy_(P0)
-        par.copy_(par0)
-        n.copy_(n0)
-
-    for _ in range(a.warmup):
-        step()
+    nph = len(w.phases)
+    for i in range(a.warmup):
+        w.step(i, ws, None, opts)
     torch.cuda.synchronize()
-    # correctness guard for the timed configuration: accepted lengths = planted
-    if plen.cpu().tolist() != c.planted["path_len"]:
-        raise RuntimeError("accepted lengths differ from the planted ones")
+    w.check()   # correctness guard for the timed configuration
+    steps = range(a.warmup, a.warmup + a.steps)
 
-    marks = [[ev() for _ in range(4)] for _ in range(a.steps)]
-    start, stop = ev(), ev()
-    torch.cuda.synchronize()
-    start.record()
-    for i in range(a.steps):
-        step(marks[i])
-    stop.record()
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
-    ms_per_step = total_ms / a.steps
-    verify_ms = [m[0].elapsed_time(m[1]) for m in marks]
-    accept_ms = [m[1].elapsed_time(m[2]) for m in marks]
-    reroot_ms = [m[2].elapsed_time(m[3]) for m in marks]
+    if a.eager:
+        # one Python call per entry point: host launch cost is inside the steps
+        marks = [[ev() for _ in range(nph + 1)] for _ in range(a.steps)]
+        start, stop = ev(), ev()
+        torch.cuda.synchronize()
+        start.record()
+        for k, i in enumerate(steps):
+            w.step(i, ws, marks[k], opts)
+        stop.record()
+        torch.cuda.synchronize()
+        ms_per_step = start.elapsed_time(stop) / a.steps
+        phase_ms = [[m[j].elapsed_time(m[j + 1]) for m in marks] for j in range(nph)]
+    else:
+        # The K steps are captured once in a HIP graph (every size the kernels
+        # need is in device memory) and replayed: the timed region is the
+        # device's work, not the Python binding's.  Each phase is timed the
+        # same way, as a graph of its K calls replayed PHASE_REPS times.
+        def capture(fn):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn()
+            return g
+
+        g_steps = capture(lambda: [w.step(i, ws, None, opts) for i in steps])
+        g_steps.replay()
+        torch.cuda.synchronize()
+        w.check()
+        start, stop = ev(), ev()
+        torch.cuda.synchronize()
+        start.record()
+        g_steps.replay()
+        stop.record()
+        torch.cuda.synchronize()
+        ms_per_step = start.elapsed_time(stop) / a.steps
+        w.check()
+        phase_ms = []
+        for j in range(nph):
+            g = capture(lambda: [w.phase(i, j, ws, opts) for i in steps])
+            g.replay()
+            per_call = []
+            for _ in range(PHASE_REPS):
+                e0, e1 = ev(), ev()
+                torch.cuda.synchronize()
+                e0.record()
+                g.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                per_call.append(e0.elapsed_time(e1) / a.steps)
+            phase_ms.append(per_call)
+            del g
+        del g_steps
+    attn_ms = phase_ms[0]
     med = lambda x: float(np.median(x))  # noqa: E731
     pct = lambda x, p: float(np.percentile(x, p))  # noqa: E731
 
-    alg = algorithmic_bytes(c)
-    v_avg_s = float(np.mean(verify_ms)) / 1e3
-    achieved = alg["total"] / v_avg_s / 1e9
-    traffic = read_traffic()
+    steps_bytes = [w.attn_bytes(i) for i in steps]
+    attn_s = float(np.mean(attn_ms)) / 1e3          # mean duration of one attention call
+    achieved = float(np.mean([b["total"] for b in steps_bytes])) / attn_s / 1e9
+    kv_gbps = float(np.mean([b["kv"] for b in steps_bytes])) / attn_s / 1e9
+    call = "tree_attn_verify" if w.phases[0] == "verify" else "4 tree_attn_expand calls"
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": traffic,
-                "kernel": "tree_attn_verify call = attention kernel + split-combine kernel",
-                "algorithmic_bytes_per_launch": alg["total"],
-                "avg_launch_us": round(v_avg_s * 1e6, 2)}
+                "traffic": read_traffic(a.workload),
+                "kernel": f"{call} (attention kernel + split-combine kernel when split)",
+                "algorithmic_bytes_per_launch": int(np.mean([b["total"] for b in steps_bytes])),
+                "avg_launch_us": round(attn_s * 1e6, 2)}
 
     _, copy_s = copy_calibration(1 << 30, 3)
     res = {
@@ -270,21 +568,21 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "chain_verify", "batch": c.B, "Hq": c.Hq, "Hkv": c.Hkv,
-                   "head_dim": c.d, "prefix": int(c.prefix_len[0]), "D": c.n_max - 1,
-                   "rows_per_kv_head": c.G * c.n_max, "vocab": c.vocab,
-                   "step": "verify + accept + re-root (+ restore of 3 tiny arrays)"},
-        "kv_read_GBps": round(alg["kv"] / v_avg_s / 1e9, 1),
-        "pct_hbm_peak": round(100 * alg["kv"] / v_avg_s / 1e9 / HBM_PEAK_GBPS, 2),
-        "verify_us": {"median": round(med(verify_ms) * 1e3, 2), "p10": round(pct(verify_ms, 10) * 1e3, 2),
-                      "p90": round(pct(verify_ms, 90) * 1e3, 2)},
-        "accept_us": round(med(accept_ms) * 1e3, 2),
-        "reroot_us": round(med(reroot_ms) * 1e3, 2),
-        "device_copy_GBps": round(2 * (1 << 30) / copy_s / 1e9, 1),
-        "roofline": roofline,
+        "config": w.config,
+        "launch": "eager (one Python call per entry point)" if a.eager else
+                  "hip_graph (the K steps captured once, replayed)",
+        "kv_read_GBps": round(kv_gbps, 1),
+        "pct_hbm_peak": round(100 * kv_gbps / HBM_PEAK_GBPS, 2),
+        f"{w.phases[0]}_us": {"median": round(med(attn_ms) * 1e3, 2),
+                              "p10": round(pct(attn_ms, 10) * 1e3, 2),
+                              "p90": round(pct(attn_ms, 90) * 1e3, 2)},
     }
+    for j in range(1, nph):
+        res[f"{w.phases[j]}_us"] = round(med(phase_ms[j]) * 1e3, 2)
+    res["device_copy_GBps"] = round(2 * (1 << 30) / copy_s / 1e9, 1)
+    res["roofline"] = roofline
     if not a.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(c, a.cpu_budget)
+        res["cpu_baseline"] = w.cpu_baseline(a.cpu_budget)
     print(json.dumps(res), flush=True)
 
 

@@ -57,11 +57,12 @@ def _threads() -> int:
     return max(1, min(16, n))
 
 
-def _normal(shape, key, dtype: str) -> np.ndarray:
+def _normal(shape, key, dtype: str, parallel: bool = True) -> np.ndarray:
     """N(0,1) array of ``shape`` drawn in rows along axis 0.
 
     Row ``r`` comes from ``default_rng(key + [r])`` so that generation can run
-    on several threads and stays identical for any thread count.
+    on several threads and stays identical for any thread count
+    (``parallel=False`` for callers that are already on a worker thread).
     """
     shape = tuple(int(s) for s in shape)
     out = np.empty(shape, dtype=np.uint16 if dtype == "bf16" else np.float32)
@@ -77,7 +78,7 @@ def _normal(shape, key, dtype: str) -> np.ndarray:
         else:
             out[r] = x.reshape(shape[1:])
 
-    if rows * per > 4_000_000:
+    if parallel and rows * per > 4_000_000:
         with ThreadPoolExecutor(_threads()) as ex:
             list(ex.map(work, range(rows)))
     else:
@@ -180,8 +181,9 @@ def _paged_kv(key, rng, B, prefix_len, n_nodes, n_max, Hkv, d, dtype, block_size
     """Paged pool with physical blocks in a seeded random order.
 
     Sequence ``b`` uses ``ceil((P_b + n_max) / block_size)`` blocks (room for
-    its tree); the tokens of sequence ``b`` are drawn in logical order from
-    ``default_rng(key + [b])`` and scattered into their blocks.
+    its tree); the keys (values) of sequence ``b`` are one stream from
+    ``default_rng(key + [21 (22), b, 0])`` in logical token order, scattered
+    into their blocks.
     """
     need = [(int(prefix_len[b]) + n_max + block_size - 1) // block_size for b in range(B)]
     total = int(sum(need)) + spare_blocks
@@ -201,8 +203,8 @@ def _paged_kv(key, rng, B, prefix_len, n_nodes, n_max, Hkv, d, dtype, block_size
     def fill(b):
         T = need[b] * block_size
         valid = int(prefix_len[b] + n_nodes[b])
-        kk = _normal((T, Hkv, d), list(key) + [21, b], dtype)
-        vv = _normal((T, Hkv, d), list(key) + [22, b], dtype)
+        kk = _normal((1, T, Hkv, d), list(key) + [21, b], dtype, parallel=False)[0]
+        vv = _normal((1, T, Hkv, d), list(key) + [22, b], dtype, parallel=False)[0]
         kk[valid:] = _nan_fill(dtype)
         vv[valid:] = _nan_fill(dtype)
         blocks = table[b, : need[b]]

@@ -4,9 +4,9 @@
 // returns the root, the accepted nodes and one new token).
 //
 // Two launches:
-//   1. argmax: one work group per (node, sequence) scans the node's logits row
-//      with 16-byte loads and a wave64 (value, index) max-reduction; ties go
-//      to the lowest index.  The result a[i] is parked in path[b][i].
+//   1. argmax: one 1024-thread work group per (node, sequence) scans the
+//      node's logits row with batches of 16-byte loads issued back to back
+//      and a wave64 (value, index) max-reduction; ties go to the lowest index.  The result a[i] is parked in path[b][i].
 //   2. path: one work group per sequence, one thread per node.  Ancestor
 //      bitmasks come from pointer doubling; "token matches the target's
 //      choice after the parent" is a wave ballot into a 256-bit mask; a node
@@ -37,9 +37,16 @@ __device__ __forceinline__ void consider(ArgMax& best, float v, int i) {
   }
 }
 
+// Loads per thread issued back to back before any of them is consumed: a row
+// of 32000 fp32 logits is 8000 16-byte vectors, under 8 per thread of a
+// 1024-thread group, so one batch of loads covers the row.
+constexpr int kArgThreads = 1024;
+constexpr int kArgUnroll = 8;
+
 template <bool kBf16>
-__global__ __launch_bounds__(kThreads) void argmax_kernel(const void* logits, const int32_t* n_nodes,
-                                                          int n_max, int V, int32_t* path) {
+__global__ __launch_bounds__(kArgThreads) void argmax_kernel(const void* logits,
+                                                             const int32_t* n_nodes, int n_max,
+                                                             int V, int32_t* path) {
   const int i = blockIdx.x;
   const int b = blockIdx.y;
   int n = n_nodes[b];
@@ -48,54 +55,57 @@ __global__ __launch_bounds__(kThreads) void argmax_kernel(const void* logits, co
   const int tid = threadIdx.x;
   ArgMax best{-INFINITY, 0x7fffffff};
   const size_t row = (static_cast<size_t>(b) * n_max + i) * static_cast<size_t>(V);
-  if (kBf16) {
-    const uint16_t* x = static_cast<const uint16_t*>(logits) + row;
-    const bool vec = (V % 8 == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
-    int start = 0;
-    if (vec) {
-      const u32x4* x4 = reinterpret_cast<const u32x4*>(x);
-      const int nv = V / 8;
-      for (int j = tid; j < nv; j += kThreads) {
-        const u32x4 w = __builtin_nontemporal_load(x4 + j);
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  constexpr int kPer = kBf16 ? 8 : 4;  // logits per 16-byte vector
+  const void* xrow = kBf16 ? static_cast<const void*>(static_cast<const uint16_t*>(logits) + row)
+                           : static_cast<const void*>(static_cast<const float*>(logits) + row);
+  const bool vec = (V % kPer == 0) && ((reinterpret_cast<uintptr_t>(xrow) & 15) == 0);
+  int start = 0;
+  if (vec) {
+    const u32x4* x4 = static_cast<const u32x4*>(xrow);
+    const int nv = V / kPer;
+    for (int base = 0; base < nv; base += kArgThreads * kArgUnroll) {
+      u32x4 w[kArgUnroll];
+#pragma unroll
+      for (int u = 0; u < kArgUnroll; ++u) {
+        const int j = base + u * kArgThreads + tid;
+        // -inf never replaces the running best (strict '>'), so padding is inert.
+        constexpr uint32_t kNegInf = kBf16 ? 0xff80ff80u : 0xff800000u;
+        w[u] = j < nv ? __builtin_nontemporal_load(x4 + j)
+                      : u32x4{kNegInf, kNegInf, kNegInf, kNegInf};
+      }
+#pragma unroll
+      for (int u = 0; u < kArgUnroll; ++u) {
+        const int j0 = (base + u * kArgThreads + tid) * kPer;
+        const uint32_t ws[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          consider(best, __uint_as_float(ws[e] << 16), 8 * j + 2 * e);
-          consider(best, __uint_as_float(ws[e] & 0xffff0000u), 8 * j + 2 * e + 1);
+          if (kBf16) {
+            consider(best, __uint_as_float(ws[e] << 16), j0 + 2 * e);
+            consider(best, __uint_as_float(ws[e] & 0xffff0000u), j0 + 2 * e + 1);
+          } else {
+            consider(best, __uint_as_float(ws[e]), j0 + e);
+          }
         }
       }
-      start = V;
     }
-    for (int j = start + tid; j < V; j += kThreads) consider(best, bf16_bits_to_f32(x[j]), j);
-  } else {
-    const float* x = static_cast<const float*>(logits) + row;
-    const bool vec = (V % 4 == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
-    int start = 0;
-    if (vec) {
-      const f32x4* x4 = reinterpret_cast<const f32x4*>(x);
-      const int nv = V / 4;
-      for (int j = tid; j < nv; j += kThreads) {
-        const f32x4 w = __builtin_nontemporal_load(x4 + j);
-        consider(best, w.x, 4 * j);
-        consider(best, w.y, 4 * j + 1);
-        consider(best, w.z, 4 * j + 2);
-        consider(best, w.w, 4 * j + 3);
-      }
-      start = V;
-    }
-    for (int j = start + tid; j < V; j += kThreads) consider(best, x[j], j);
+    start = V;
+  }
+  for (int j = start + tid; j < V; j += kArgThreads) {
+    const float x = kBf16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(xrow)[j])
+                          : static_cast<const float*>(xrow)[j];
+    consider(best, x, j);
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     ArgMax other{__shfl_xor(best.v, o, 64), __shfl_xor(best.i, o, 64)};
     best = better(best, other);
   }
-  __shared__ ArgMax sBest[kThreads / 64];
+  __shared__ ArgMax sBest[kArgThreads / 64];
   if ((tid & 63) == 0) sBest[tid >> 6] = best;
   __syncthreads();
   if (tid == 0) {
     ArgMax r = sBest[0];
-    for (int w = 1; w < kThreads / 64; ++w) r = better(r, sBest[w]);
+    for (int w = 1; w < kArgThreads / 64; ++w) r = better(r, sBest[w]);
     // Every row has at least one element; an all-NaN row reports index 0.
     path[static_cast<size_t>(b) * n_max + i] = (r.i == 0x7fffffff) ? 0 : r.i;
   }
@@ -187,8 +197,8 @@ hipError_t launch_accept(const void* logits, int logit_dtype, const int32_t* par
                          int32_t* bonus, hipStream_t s) {
   dim3 g1(n_max, B);
   hipError_t e = logit_dtype == TA_BF16
-                     ? launch(argmax_kernel<true>, g1, dim3(kThreads), s, logits, n_nodes, n_max, V, path)
-                     : launch(argmax_kernel<false>, g1, dim3(kThreads), s, logits, n_nodes, n_max, V, path);
+                     ? launch(argmax_kernel<true>, g1, dim3(kArgThreads), s, logits, n_nodes, n_max, V, path)
+                     : launch(argmax_kernel<false>, g1, dim3(kArgThreads), s, logits, n_nodes, n_max, V, path);
   if (e != hipSuccess) return e;
   return launch(accept_path_kernel, dim3(B), dim3(kThreads), s, parent, tok, n_nodes, root_tok,
                 n_max, path, path_len, bonus);

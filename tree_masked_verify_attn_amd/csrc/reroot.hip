@@ -3,13 +3,15 @@
 // under the last verified node is pulled forward to follow it, the rest is
 // dropped; KV is moved, never recomputed).
 //
-// Launch 1 (move): one work group per (KV head, K|V, sequence x layer).  The
-// group rebuilds the move list itself from parent/path/keep (ancestor masks by
-// pointer doubling, kept-node ranks by popcount), then copies every moved row
-// of its own (layer, K|V, head) column slice: all rows are loaded into
-// registers, the group synchronises, then all rows are stored.  Because a
-// group owns its slice exclusively, a destination row that is another move's
-// source is never overwritten before it has been read.
+// Launch 1 (move): one work group per (KV head x 64-byte column slice, K|V,
+// sequence x layer).  The group rebuilds the move list itself from
+// parent/path/keep (ancestor masks by pointer doubling, kept-node ranks by
+// popcount); if no row changes place (a chain, or a path that is already in
+// order) it stops there.  Otherwise it copies its own 64-byte slice of every
+// moved row: all loads go to registers (at most 4 x 16 bytes per thread), the
+// group synchronises, then all stores run.  Because a group owns its slice
+// exclusively, a destination that is another move's source is never
+// overwritten before it has been read.
 // Launch 2 (metadata): one work group per sequence rewrites parent, n_nodes
 // and prefix_len after every layer has been moved (stream order).
 #include "ta_device.h"
@@ -18,7 +20,8 @@ namespace ta {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMaxChunksPerThread = 32;  // 256 rows x 512 B / (256 threads x 16 B)
+constexpr int kSliceChunks = 4;  // 16-byte chunks per column slice (64 bytes)
+constexpr int kMaxChunksPerThread = kMaxNodes * kSliceChunks / kThreads;
 
 struct Plan {
   int P, n, k, keep, v_last, n_kept, valid;
@@ -84,7 +87,9 @@ __global__ __launch_bounds__(kThreads) void reroot_move_kernel(
   __shared__ int sSrc[kMaxNodes];
   __shared__ int sDst[kMaxNodes];
 
-  const int hkv = blockIdx.x;
+  const int n_slices = row_bytes / (16 * kSliceChunks);
+  const int hkv = blockIdx.x / n_slices;
+  const int slice = blockIdx.x % n_slices;
   const int which = blockIdx.y;  // 0: K, 1: V
   const int b = blockIdx.z / n_layers;
   const int layer = blockIdx.z % n_layers;
@@ -109,10 +114,10 @@ __global__ __launch_bounds__(kThreads) void reroot_move_kernel(
     }
   }
   __syncthreads();
+  if (!__syncthreads_or(tid < n_moves && sSrc[tid] != sDst[tid])) return;
 
-  const int cpr = row_bytes / 16;  // 16-byte chunks per row
-  const int total = n_moves * cpr;
-  uint8_t* base = static_cast<uint8_t*>(which == 0 ? L.k : L.v);
+  const int total = n_moves * kSliceChunks;
+  uint8_t* base = static_cast<uint8_t*>(which == 0 ? L.k : L.v) + slice * (16 * kSliceChunks);
   const bool paged = L.block_table != nullptr;
   const int cap = paged ? L.max_blocks * L.block_size : L.T_cap;
   auto row_ptr = [&](int pos) -> uint8_t* {
@@ -127,28 +132,34 @@ __global__ __launch_bounds__(kThreads) void reroot_move_kernel(
     return base + row * static_cast<size_t>(row_bytes);
   };
 
-  uint4 buf[kMaxChunksPerThread];
-#pragma unroll
-  for (int c = 0; c < kMaxChunksPerThread; ++c) {
+  // Element e = tid + c * kThreads of the move list: row e / kSliceChunks,
+  // chunk e % kSliceChunks of the slice.  Four named registers (not an array,
+  // which the compiler places in scratch memory).
+  static_assert(kMaxChunksPerThread == 4, "one register per chunk below");
+  auto src_of = [&](int c, int& m, int& ch) {
     const int e = tid + c * kThreads;
-    if (e < total) {
-      const int m = e / cpr, ch = e % cpr;
-      const int src = sSrc[m], dst = sDst[m];
-      if (src != dst && src < cap && dst < cap)
-        buf[c] = *reinterpret_cast<const uint4*>(row_ptr(src) + ch * 16);
-    }
-  }
+    m = e / kSliceChunks;
+    ch = e % kSliceChunks;
+    return e < total && sSrc[m] != sDst[m] && sSrc[m] < cap && sDst[m] < cap;
+  };
+  auto load = [&](int c, uint4& r) {
+    int m, ch;
+    if (src_of(c, m, ch)) r = *reinterpret_cast<const uint4*>(row_ptr(sSrc[m]) + ch * 16);
+  };
+  auto store = [&](int c, const uint4& r) {
+    int m, ch;
+    if (src_of(c, m, ch)) *reinterpret_cast<uint4*>(row_ptr(sDst[m]) + ch * 16) = r;
+  };
+  uint4 r0 = {}, r1 = {}, r2 = {}, r3 = {};
+  load(0, r0);
+  load(1, r1);
+  load(2, r2);
+  load(3, r3);
   __syncthreads();
-#pragma unroll
-  for (int c = 0; c < kMaxChunksPerThread; ++c) {
-    const int e = tid + c * kThreads;
-    if (e < total) {
-      const int m = e / cpr, ch = e % cpr;
-      const int src = sSrc[m], dst = sDst[m];
-      if (src != dst && src < cap && dst < cap)
-        *reinterpret_cast<uint4*>(row_ptr(dst) + ch * 16) = buf[c];
-    }
-  }
+  store(0, r0);
+  store(1, r1);
+  store(2, r2);
+  store(3, r3);
 }
 
 __global__ __launch_bounds__(kThreads) void reroot_meta_kernel(int32_t* prefix_len,
@@ -188,7 +199,8 @@ hipError_t launch_reroot_move(const RerootLayers& layers, int n_layers, const in
                               const int32_t* parent, const int32_t* n_nodes, const int32_t* path,
                               const int32_t* path_len, const uint8_t* keep, int B, int n_max,
                               int Hkv, int row_bytes, hipStream_t s) {
-  dim3 grid(Hkv, 2, B * n_layers);
+  // row_bytes is 128, 256 or 512 (d = 64 or 128, bf16 or fp32): whole slices.
+  dim3 grid(Hkv * (row_bytes / (16 * kSliceChunks)), 2, B * n_layers);
   return launch(reroot_move_kernel, grid, dim3(kThreads), s, layers, n_layers, prefix_len, parent,
                 n_nodes, path, path_len, keep, n_max, Hkv, row_bytes);
 }
