@@ -17,6 +17,7 @@ namespace ta {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kBatch = 4;  // partial states in flight per thread
 constexpr float kLn2 = 0.69314718055994530942f;
 
 template <typename T>
@@ -59,17 +60,40 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(AttnParams p) {
   if (node < 0 || node >= sb.n) return;
 
   const size_t part = static_cast<size_t>(bh * p.n_row_tiles + rtile) * p.n_split;
-  float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s)
-    M = fmaxf(M, p.ws_ml[((part + s) * p.rows_per_tile + r) * 2]);
-  float L = 0.f;
+  // Partial states are read kBatch at a time with unconditional loads (splits
+  // past the last repeat it and get weight zero), so that a batch's loads are
+  // all in flight before the first is used; batches combine online.
+  float M = -INFINITY, L = 0.f;
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < nsplit; ++s) {
-    const size_t pr = (part + s) * p.rows_per_tile + r;
-    const float ms = p.ws_ml[pr * 2];
-    const float wgt = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
-    L = fmaf(p.ws_ml[pr * 2 + 1], wgt, L);
-    o += *reinterpret_cast<const f32x4*>(p.ws_o + pr * p.d + 4 * dg) * wgt;
+  for (int s0 = 0; s0 < nsplit; s0 += kBatch) {
+    float ms[kBatch], ls[kBatch];
+    f32x4 os[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int sp = s0 + k < nsplit ? s0 + k : nsplit - 1;
+      const size_t pr = (part + sp) * p.rows_per_tile + r;
+      const float2 ml = *reinterpret_cast<const float2*>(p.ws_ml + pr * 2);
+      ms[k] = ml.x;
+      ls[k] = ml.y;
+      os[k] = *reinterpret_cast<const f32x4*>(p.ws_o + pr * p.d + 4 * dg);
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k)
+      if (s0 + k >= nsplit) ms[k] = -INFINITY;
+    float Mb = M;
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) Mb = fmaxf(Mb, ms[k]);
+    if (Mb == -INFINITY) continue;  // no visible position so far
+    const float a = (M == -INFINITY) ? 0.f : exp2f(M - Mb);
+    L *= a;
+    o *= a;
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const float wgt = (ms[k] == -INFINITY) ? 0.f : exp2f(ms[k] - Mb);
+      L = fmaf(ls[k], wgt, L);
+      o += os[k] * wgt;
+    }
+    M = Mb;
   }
   const float inv = 1.f / L;
   T* out = static_cast<T*>(p.out) +

@@ -164,19 +164,24 @@ __global__ __launch_bounds__(kThreads, S == 3 ? 3 : 2) void attn_stream_kernel(A
     __syncthreads();  // the ring may now overwrite the ancestor table
   }
 
-  const uint16_t* Q = static_cast<const uint16_t*>(p.q);
-  const size_t qrow = ((static_cast<size_t>(b) * p.n_q + slot) * p.Hq + hkv * p.G + g) * D;
+  // Q^T operand (B side of S^T = K . Q^T): lane holds row l32, chunk 2*ks + lhi.
+  // Loaded once the first ring stages are in flight (below), so that both
+  // latencies overlap.
   bf16x8 qreg[C::KS];
+  auto load_q = [&]() {
+    const uint16_t* Q = static_cast<const uint16_t*>(p.q);
+    const size_t qrow = ((static_cast<size_t>(b) * p.n_q + slot) * p.Hq + hkv * p.G + g) * D;
 #pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) {
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (node >= 0) v = *reinterpret_cast<const u32x4*>(Q + qrow + (2 * ks + lhi) * 8);
-    qreg[ks] = __builtin_bit_cast(bf16x8, v);
-  }
-  // Complete the Q loads with a wait the compiler can see (vmcnt(0), other
-  // counters untouched); otherwise it would re-wait for them inside the ring
-  // loop, where the outstanding loads are the ring's.
-  __builtin_amdgcn_s_waitcnt(0x0F70);
+    for (int ks = 0; ks < C::KS; ++ks) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (node >= 0) v = *reinterpret_cast<const u32x4*>(Q + qrow + (2 * ks + lhi) * 8);
+      qreg[ks] = __builtin_bit_cast(bf16x8, v);
+    }
+    // Complete every load with a wait the compiler can see (vmcnt(0), other
+    // counters untouched); otherwise it would re-wait for the Q loads inside
+    // the ring loop, where the outstanding loads are the ring's.
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+  };
 
   // ---- ring of stages ----------------------------------------------------
   const uint8_t* Kg = static_cast<const uint8_t*>(p.k);
@@ -344,8 +349,9 @@ __global__ __launch_bounds__(kThreads, S == 3 ? 3 : 2) void attn_stream_kernel(A
     if (j >= 1 && j + S - 2 < ntiles) issue_stage(j + S - 2, (slot + S - 2) % S);
   };
 
-  // Prologue: stages 0 .. S-2 in flight, tile 0's scores started.
+  // Prologue: stages 0 .. S-2 and the queries in flight, tile 0's scores started.
   for (int j = 0; j < S - 1 && j < ntiles; ++j) issue_stage(j, j);
+  load_q();
   arrive(0, 0);
   f32x16 s_cur = rg >= 0 ? qk(0) : f32x16{};
   // Iteration j: tile j+1 arrives and its scores start on the matrix cores,
@@ -365,17 +371,25 @@ __global__ __launch_bounds__(kThreads, S == 3 ? 3 : 2) void attn_stream_kernel(A
       }
     }
   }
-  for (; j < ntiles; ++j) {
-    const bool more = j + 1 < ntiles;
-    if (more) arrive(j + 1, (j + 1) % S);
-    if (rg >= 0) {
-      f32x16 s_next = {};
-      if (more) s_next = qk((j + 1) % S);
-      if (j < n_clean)
-        softmax_pv(s_cur, j, j % S, std::false_type{});
-      else
-        softmax_pv(s_cur, j, j % S, std::true_type{});
-      s_cur = s_next;
+  // The rest (the masked tail, the last tiles), unrolled the same way: j is a
+  // multiple of S here, so tile j + u sits in slot u.
+  for (; j < ntiles; j += S) {
+#pragma unroll
+    for (int u = 0; u < S; ++u) {
+      const int jj = j + u;
+      if (jj < ntiles) {
+        const bool more = jj + 1 < ntiles;
+        if (more) arrive(jj + 1, (u + 1) % S);
+        if (rg >= 0) {
+          f32x16 s_next = {};
+          if (more) s_next = qk((u + 1) % S);
+          if (jj < n_clean)
+            softmax_pv(s_cur, jj, u, std::false_type{});
+          else
+            softmax_pv(s_cur, jj, u, std::true_type{});
+          s_cur = s_next;
+        }
+      }
     }
   }
   wait_vmcnt<0>();
