@@ -63,7 +63,7 @@ int round_up(int x, int m) { return (x + m - 1) / m * m; }
 // chunk gives about two work groups per compute unit, never below 256 KV
 // positions per split (smaller chunks cost more in partial results than they
 // gain in parallelism).
-bool make_plan(int B, int n_q, int Hq, int Hkv, int d, int dtype, int T_cap,
+bool make_plan(int B, int n_q, int Hq, int Hkv, int d, int dtype, int T_cap, bool paged,
                const ta_attn_opts* opts, Plan& pl) {
   const int G = Hq / Hkv;
   const int R = n_q * G;
@@ -83,7 +83,13 @@ bool make_plan(int B, int n_q, int Hq, int Hkv, int d, int dtype, int T_cap,
   int chunk = opts ? opts->chunk_tokens : 0;
   if (chunk < 0 || chunk % 64 != 0) return false;
   if (chunk == 0) {
-    const long long want = 2LL * device_cu_count();
+    // A contiguous cache gives every sequence one capacity, the usual layout
+    // for sequences of equal length: one split per resident work group (two
+    // per compute unit).  A paged cache usually holds sequences of mixed
+    // lengths, whose actual lengths only the device knows: four times as many
+    // splits as resident groups, so that the hardware dispatcher balances
+    // long and short sequences as groups finish.
+    const long long want = (paged ? 8LL : 2LL) * device_cu_count();
     long long splits = items > 0 ? (want + items - 1) / items : 1;
     splits = std::max(1LL, splits);
     chunk = round_up(static_cast<int>((T_cap + splits - 1) / splits), 64);
@@ -96,6 +102,8 @@ bool make_plan(int B, int n_q, int Hq, int Hkv, int d, int dtype, int T_cap,
   pl.chunk = chunk;
   pl.n_split = (T_cap + chunk - 1) / chunk;
   if (pl.n_split < 1) pl.n_split = 1;
+  // launch limits: splits and row tiles are grid y / z (at most 65535 each)
+  if (pl.n_split > 65535 || pl.n_row_tiles > 65535) return false;
   const long long tiles = static_cast<long long>(B) * Hkv * pl.n_row_tiles;
   pl.ws_bytes = ta::attn_ws_bytes(static_cast<int>(tiles), pl.n_split, pl.rows_per_tile, d);
   return true;
@@ -134,7 +142,8 @@ int run_attention(const void* q, ta_kv kv, const int32_t* prefix_len, const int3
   if (!(scale > 0.f) || scale != scale) return TA_ERR_INVALID_ARG;
   if (B == 0) return TA_OK;
   Plan pl;
-  if (!make_plan(B, n_q, Hq, Hkv, d, dtype, kv.T_cap, opts, pl)) return TA_ERR_UNSUPPORTED;
+  if (!make_plan(B, n_q, Hq, Hkv, d, dtype, kv.T_cap, kv.block_table != nullptr, opts, pl))
+    return TA_ERR_UNSUPPORTED;
   if (pl.kernel != 1 && !(aligned16(q) && aligned16(out) && aligned16(kv.k) && aligned16(kv.v)))
     return TA_ERR_INVALID_ARG;
   // The streaming kernel keeps one split's paged block ids in LDS; when they do
@@ -208,8 +217,12 @@ size_t tree_attn_workspace_bytes(int B, int n_q, int Hq, int Hkv, int d, int dty
   if (check_common(B, n_q, n_q, Hq, Hkv, d, dtype, T_cap) != TA_OK) return static_cast<size_t>(-1);
   if (B == 0) return 0;
   Plan pl;
-  if (!make_plan(B, n_q, Hq, Hkv, d, dtype, T_cap, opts, pl)) return static_cast<size_t>(-1);
-  return pl.ws_bytes;
+  // enough for either layout's plan
+  Plan pp;
+  if (!make_plan(B, n_q, Hq, Hkv, d, dtype, T_cap, false, opts, pl) ||
+      !make_plan(B, n_q, Hq, Hkv, d, dtype, T_cap, true, opts, pp))
+    return static_cast<size_t>(-1);
+  return std::max(pl.ws_bytes, pp.ws_bytes);
 }
 
 int tree_attn_verify(const void* q, ta_kv kv, const int32_t* prefix_len, const int32_t* parent,

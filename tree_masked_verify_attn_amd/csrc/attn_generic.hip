@@ -7,7 +7,7 @@
 // node i, query head h) softmax attention over the P prefix positions and the
 // tree positions of i's ancestors and i itself, with KV head h / G.
 //
-// Work decomposition: one work group per (split, row tile, sequence x KV head).
+// Work decomposition: one work group per (sequence x KV head, split, row tile).
 // A row tile is 32 query rows (node-major, the G heads of a node adjacent);
 // a split is `chunk` consecutive KV positions.  Each of the 4 waves owns 8
 // rows; a 64-position K/V tile is staged in LDS as fp32, lane j scores
@@ -52,9 +52,13 @@ __global__ __launch_bounds__(kThreads) void attn_generic_kernel(AttnParams p) {
   __shared__ int sJump[kMaxNodes];
   __shared__ int sNode[kRows];
 
-  const int split = blockIdx.x;
-  const int rtile = blockIdx.y;
-  const int bh = blockIdx.z;
+  // grid = (sequence x KV head, split, row tile): consecutive work groups are
+  // different (sequence, KV head) pairs, which the dispatcher deals round
+  // robin to the eight XCDs, so every XCD gets an even share of every split
+  // (with the split fastest, split s of all sequences would land on one XCD).
+  const int bh = blockIdx.x;
+  const int split = blockIdx.y;
+  const int rtile = blockIdx.z;
   const int b = bh / p.Hkv;
   const int hkv = bh % p.Hkv;
   const int tid = threadIdx.x;
@@ -219,7 +223,7 @@ __global__ __launch_bounds__(kThreads) void attn_generic_kernel(AttnParams p) {
 }  // namespace
 
 hipError_t launch_attn_generic(const AttnParams& p, int dtype, hipStream_t s) {
-  dim3 grid(p.n_split, p.n_row_tiles, p.B * p.Hkv);
+  dim3 grid(p.B * p.Hkv, p.n_split, p.n_row_tiles);
   dim3 block(kThreads);
   if (dtype == TA_F32)
     return p.d == 64 ? launch(attn_generic_kernel<float, 64>, grid, block, s, p)

@@ -34,11 +34,11 @@ __device__ __forceinline__ void store4<uint16_t>(uint16_t* out, f32x4 v) {
   *reinterpret_cast<u32x2*>(out) = u32x2{lo, hi};
 }
 
-// grid = (row-tile x channel-group blocks, sequence x KV head); one thread
+// grid = (sequence x KV head, row-tile x channel-group blocks); one thread
 // per (row, 4 channels) of a tile.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void merge_kernel(AttnParams p) {
-  const int bh = blockIdx.y;
+  const int bh = blockIdx.x;
   const int b = bh / p.Hkv;
   const int hkv = bh % p.Hkv;
   SeqBounds sb;
@@ -47,7 +47,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(AttnParams p) {
   if (nsplit <= 1) return;  // the attention kernel wrote this sequence's results
   const int groups = p.d / 4;
   const int per_tile = p.rows_per_tile * groups;
-  const int e = blockIdx.x * kThreads + threadIdx.x;
+  const int e = blockIdx.y * kThreads + threadIdx.x;
   const int rtile = e / per_tile;
   if (rtile >= p.n_row_tiles) return;
   const int r = (e % per_tile) / groups;
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(AttnParams p) {
 
 hipError_t launch_attn_merge(const AttnParams& p, int dtype, hipStream_t s) {
   const long long items = static_cast<long long>(p.n_row_tiles) * p.rows_per_tile * (p.d / 4);
-  const dim3 grid(static_cast<unsigned>((items + kThreads - 1) / kThreads), p.B * p.Hkv);
+  const dim3 grid(p.B * p.Hkv, static_cast<unsigned>((items + kThreads - 1) / kThreads));
   if (dtype == TA_F32) return launch(merge_kernel<float>, grid, dim3(kThreads), s, p);
   return launch(merge_kernel<uint16_t>, grid, dim3(kThreads), s, p);
 }

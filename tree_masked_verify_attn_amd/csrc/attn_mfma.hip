@@ -10,7 +10,7 @@
 // per-row ancestor bitmask.
 //
 // Layout of the work (one work group = 4 waves of 64 lanes):
-//  * grid = (split, row tile, sequence x KV head); a split is `chunk` KV
+//  * grid = (sequence x KV head, split, row tile); a split is `chunk` KV
 //    positions; a row tile is 32 x NRG query rows (NRG = 1..4 row groups).
 //  * Each wave owns one 32-row group and a share of every LDS tile's tokens
 //    (with NRG < 4 several waves share a row group and split the tile's
@@ -89,9 +89,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnParams p) {
   uint8_t* sK = sKV;
   uint8_t* sV = sKV + C::TILE_BYTES;
 
-  const int split = blockIdx.x;
-  const int rtile = blockIdx.y;
-  const int bh = blockIdx.z;
+  // grid = (sequence x KV head, split, row tile): consecutive work groups are
+  // different (sequence, KV head) pairs, which the dispatcher deals round
+  // robin to the eight XCDs, so every XCD gets an even share of every split
+  // (with the split fastest, split s of all sequences would land on one XCD).
+  const int bh = blockIdx.x;
+  const int split = blockIdx.y;
+  const int rtile = blockIdx.z;
   const int b = bh / p.Hkv;
   const int hkv = bh % p.Hkv;
   const int tid = threadIdx.x;
@@ -364,7 +368,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnParams p) {
 
 template <int D>
 hipError_t launch_d(const AttnParams& p, hipStream_t s) {
-  dim3 grid(p.n_split, p.n_row_tiles, p.B * p.Hkv);
+  dim3 grid(p.B * p.Hkv, p.n_split, p.n_row_tiles);
   const dim3 block(kThreads);
   switch (p.rows_per_tile / 32) {
     case 1: return launch(attn_mfma_kernel<D, 1>, grid, block, s, p);

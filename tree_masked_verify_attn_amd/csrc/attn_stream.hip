@@ -110,9 +110,13 @@ __global__ __launch_bounds__(kThreads, S == 3 ? 3 : 2) void attn_stream_kernel(A
   __shared__ int sBlk[kMaxSplitBlocks];
   __shared__ uint64_t sRowMask[C::RPT][kMaskWords];  // ancestor mask of each row's node
 
-  const int split = blockIdx.x;
-  const int rtile = blockIdx.y;
-  const int bh = blockIdx.z;
+  // grid = (sequence x KV head, split, row tile): consecutive work groups are
+  // different (sequence, KV head) pairs, which the dispatcher deals round
+  // robin to the eight XCDs, so every XCD gets an even share of every split
+  // (with the split fastest, split s of all sequences would land on one XCD).
+  const int bh = blockIdx.x;
+  const int split = blockIdx.y;
+  const int rtile = blockIdx.z;
   const int b = bh / p.Hkv;
   const int hkv = bh % p.Hkv;
   const int tid = threadIdx.x;
@@ -440,7 +444,7 @@ __global__ __launch_bounds__(kThreads, S == 3 ? 3 : 2) void attn_stream_kernel(A
 
 template <int D, int S>
 hipError_t launch_ds(const AttnParams& p, hipStream_t s) {
-  const dim3 grid(p.n_split, p.n_row_tiles, p.B * p.Hkv);
+  const dim3 grid(p.B * p.Hkv, p.n_split, p.n_row_tiles);
   const dim3 block(kThreads);
   switch (p.rows_per_tile / 32) {
     case 1: return launch(attn_stream_kernel<D, 1, S>, grid, block, s, p);
