@@ -181,6 +181,38 @@ int tree_cache_reroot(const ta_kv* kv_layers, int n_layers, int32_t* prefix_len,
                       const uint8_t* keep_subtree, int B, int n_max, int Hkv, int d, int dtype,
                       void* stream);
 
+/*
+ * Maximum-likelihood draft-tree expansion step ([SS] Section 3.1.3: a node's
+ * value is the log-softmax probability of its token under its parent's
+ * distribution, its weight the sum of the values from the root down to it;
+ * an expansion takes the w best new leaves).
+ *
+ *   logits   [B][n_max + 1][V] fp32 or bf16 (logit_dtype): row 0 is the draft
+ *            distribution after the root (the last prefix token), row 1 + i
+ *            the one after node i
+ *   parent   [B][n_max] int32 in/out, tok [B][n_max] int32 in/out,
+ *   cum      [B][n_max] fp32 in/out: weight (cumulative log-probability) of
+ *            each node, which the caller keeps for the existing nodes
+ *   n_nodes  [B] int32 in/out
+ *
+ * For each sequence with n = n_nodes[b] the candidates are the pairs (p, t)
+ * with p in {-1 (root), 0 .. n-1} and t a token (0 <= t < V) that is not
+ * already the token of a child of p.  Candidate (p, t) scores
+ *     cum[p] + logits[b][p + 1][t] - log sum_v exp(logits[b][p + 1][v])
+ * (cum[-1] = 0), computed in fp32.  The best min(w, n_max - n) candidates
+ * (higher score first; ties: lower p, then higher logit, then lower t)
+ * become nodes n, n+1, ...: parent, tok and cum are written there and
+ * n_nodes[b] grows by their number.  Logits must be finite.  1 <= w <= 16,
+ * V <= 262144; ws holds tree_expand_top_w_workspace_bytes bytes (no
+ * initialisation needed; calls that overlap in time must not share it).
+ */
+int tree_expand_top_w(const void* logits, int logit_dtype, int32_t* parent, int32_t* tok,
+                      float* cum, int32_t* n_nodes, int B, int n_max, int V, int w, void* ws,
+                      size_t ws_bytes, void* stream);
+
+/* Workspace (bytes) for tree_expand_top_w, or (size_t)-1 for invalid sizes. */
+size_t tree_expand_top_w_workspace_bytes(int B, int n_max, int w);
+
 /* Human-readable name of a ta_status value (static string). */
 const char* ta_status_string(int status);
 

@@ -106,6 +106,26 @@ def test_invalid_arguments_are_rejected_on_the_host():
     assert st == _lib.TA_ERR_INVALID_ARG
 
 
+def test_top_w_host_side_validation():
+    """tree_expand_top_w rejects bad sizes before touching device memory."""
+    lib = ensure_built()
+    call = lambda B=2, n_max=16, V=100, w=4, dt=ta.TA_F32, ws=0xa000, wsb=1 << 20: \
+        lib.tree_expand_top_w(0x1000, dt, 0x2000, 0x3000, 0x4000, 0x5000, B, n_max, V, w, ws,
+                              wsb, None)  # noqa: E731
+    assert call(w=0) == _lib.TA_ERR_INVALID_ARG
+    assert call(w=17) == _lib.TA_ERR_UNSUPPORTED
+    assert call(V=(1 << 18) + 1) == _lib.TA_ERR_UNSUPPORTED
+    assert call(n_max=257) == _lib.TA_ERR_TREE_TOO_LARGE
+    assert call(dt=9) == _lib.TA_ERR_UNSUPPORTED
+    assert call(ws=None) == _lib.TA_ERR_WORKSPACE
+    need = ta.tree_expand_top_w_workspace_bytes(2, 16, 4)
+    assert need == 2 * 17 * 4 * 8
+    assert call(wsb=need - 1) == _lib.TA_ERR_WORKSPACE
+    assert call(B=0) == _lib.TA_OK
+    with pytest.raises(ta.TreeAttnError):
+        ta.tree_expand_top_w_workspace_bytes(1, 16, 0)
+
+
 def test_workspace_query_rejects_bad_sizes():
     ensure_built()
     with pytest.raises(ta.TreeAttnError):

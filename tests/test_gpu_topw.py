@@ -1,0 +1,168 @@
+"""GPU parity of tree_expand_top_w against the float64 oracle (oracle/topw.py).
+
+The kernel scores candidates in fp32, the oracle in fp64, so which candidates
+win is compared exactly only where the fp64 scores are separated by more than
+the fp32 error; within that margin any of the near-equal candidates is a
+correct pick, and the test checks the picks are valid and in order instead.
+The cumulative scores written for the new nodes are compared with the fp64
+scores of the same candidates."""
+import numpy as np
+import pytest
+
+from helpers import dev_tensor, ensure_built
+
+import oracle
+from oracle.topw import log_softmax
+from gen import config4_expand, random_case
+
+pytestmark = pytest.mark.gpu
+
+SCORE_TOL = 2e-4  # fp32 log-softmax of a 32000-way row: a few 1e-6 relative
+
+
+@pytest.fixture(scope="module")
+def ta():
+    ensure_built()
+    import tree_masked_verify_attn_amd as m
+    return m
+
+
+def _fp64_scores(parent, tok, cum, logits, n):
+    """Every candidate's fp64 score: dict (p, t) -> score (p = -1 is the root)."""
+    V = logits.shape[1]
+    out = {}
+    for p in range(-1, n):
+        row = logits[p + 1].astype(np.float64)
+        lsm = log_softmax(row)
+        base = 0.0 if p < 0 else float(cum[p])
+        taken = {int(tok[c]) for c in range(n) if int(parent[c]) == p}
+        for t in range(V):
+            if t not in taken:
+                out[(p, t)] = base + lsm[t]
+    return out
+
+
+def _check_round(par0, tok0, cum0, n0, logits, w, n_max, par1, tok1, cum1, n1):
+    """One sequence's expansion step: GPU result (…1) against the oracle."""
+    take = min(w, n_max - n0)
+    assert n1 == n0 + take
+    # existing nodes untouched
+    np.testing.assert_array_equal(par1[:n0], par0[:n0])
+    np.testing.assert_array_equal(tok1[:n0], tok0[:n0])
+    if take == 0:
+        return
+    # one more than taken, to see the margin at the boundary
+    P, T, S = oracle.select_top_w(par0, tok0, cum0.astype(np.float64), logits[0], logits[1:], n0,
+                                  take + 1)
+    got = [(int(par1[n0 + k]), int(tok1[n0 + k])) for k in range(take)]
+    want = [(int(P[k]), int(T[k])) for k in range(take)]
+    separated = all(S[k] - S[k + 1] > SCORE_TOL for k in range(len(S) - 1))
+    if separated:
+        assert got == want
+        np.testing.assert_allclose(cum1[n0:n0 + take], S[:take], rtol=1e-5, atol=SCORE_TOL)
+        return
+    # near ties: the picks must be valid, distinct, ordered and as good as the oracle's
+    scores = _fp64_scores(par0, tok0, cum0, logits, n0)
+    assert len(set(got)) == take
+    s_got = np.array([scores[g] for g in got])       # KeyError = a taken token was picked
+    assert np.all(np.diff(s_got) <= SCORE_TOL)
+    assert s_got[-1] >= S[take - 1] - SCORE_TOL
+    np.testing.assert_allclose(cum1[n0:n0 + take], s_got, rtol=1e-5, atol=SCORE_TOL)
+
+
+def _run(ta, logits, par, tok, cum, n, w, dtype="f32"):
+    import torch
+    lg = dev_tensor(logits)
+    if dtype == "bf16":
+        lg = lg.to(torch.bfloat16)
+    d_par, d_tok = dev_tensor(par.copy()), dev_tensor(tok.copy())
+    d_cum, d_n = dev_tensor(cum.astype(np.float32).copy()), dev_tensor(n.astype(np.int32).copy())
+    ta.tree_expand_top_w(lg, d_par, d_tok, d_cum, d_n, w)
+    torch.cuda.synchronize()
+    return (d_par.cpu().numpy(), d_tok.cpu().numpy(), d_cum.cpu().numpy(), d_n.cpu().numpy(),
+            lg.float().cpu().numpy())
+
+
+@pytest.mark.parametrize("seed,V,w,dtype", [
+    (1, 50, 4, "f32"), (2, 1000, 8, "f32"), (3, 32000, 8, "f32"), (4, 32000, 16, "bf16"),
+    (5, 777, 1, "f32"), (6, 4096, 12, "bf16"), (7, 33, 16, "f32")])
+def test_topw_random_trees(ta, seed, V, w, dtype):
+    c = random_case(seed, B=3, Hq=1, Hkv=1, d=64, P_range=(0, 2), n_max=40, n_range=(1, 30),
+                    dtype="f32", vocab=V)
+    rng = np.random.default_rng([seed, 7])
+    logits = rng.standard_normal((c.B, c.n_max + 1, V), dtype=np.float32)
+    cum = np.zeros((c.B, c.n_max), dtype=np.float32)
+    for b in range(c.B):
+        n = int(c.n_nodes[b])
+        lg = logits[b].astype(np.float64)
+        if dtype == "bf16":
+            import torch
+            lg = torch.from_numpy(logits[b]).to(torch.bfloat16).float().numpy().astype(np.float64)
+        cum[b, :n] = oracle.cumulative_scores(c.parent[b], c.tok[b], lg[0], lg[1:], n)
+    par1, tok1, cum1, n1, lg_used = _run(ta, logits, c.parent, c.tok, cum, c.n_nodes, w, dtype)
+    for b in range(c.B):
+        _check_round(c.parent[b], c.tok[b], cum[b], int(c.n_nodes[b]), lg_used[b], w, c.n_max,
+                     par1[b], tok1[b], cum1[b], int(n1[b]))
+
+
+def test_topw_excludes_existing_children_and_capacity(ta):
+    """The best logits of a row belong to existing children: they must not be
+    picked again; a nearly full tree appends only up to n_max."""
+    V, n_max = 500, 12
+    parent = np.array([[-1, -1, 0, 0, 1, 2, -1, -1, -1, -1, -1, -1],
+                       [-1, 0, 1, 2, 3, 4, 5, 6, 7, 8, -1, -1]], dtype=np.int32)
+    tok = np.array([[5, 6, 7, 8, 9, 10, 0, 0, 0, 0, 0, 0],
+                    [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 0, 0]], dtype=np.int32)
+    n = np.array([6, 10], dtype=np.int32)
+    rng = np.random.default_rng(3)
+    logits = rng.standard_normal((2, n_max + 1, V), dtype=np.float32)
+    for b in range(2):
+        for c in range(int(n[b])):
+            logits[b, parent[b, c] + 1, tok[b, c]] = 9.0     # children hold their row's maximum
+    cum = np.zeros((2, n_max), dtype=np.float32)
+    for b in range(2):
+        cum[b, :n[b]] = oracle.cumulative_scores(parent[b], tok[b], logits[b, 0], logits[b, 1:],
+                                                 int(n[b]))
+    par1, tok1, cum1, n1, lg = _run(ta, logits, parent, tok, cum, n, 4)
+    assert n1.tolist() == [10, 12]
+    for b in range(2):
+        _check_round(parent[b], tok[b], cum[b], int(n[b]), lg[b], 4, n_max, par1[b], tok1[b],
+                     cum1[b], int(n1[b]))
+        for k in range(int(n[b]), int(n1[b])):
+            sib = [int(tok1[b, c]) for c in range(int(n1[b])) if par1[b, c] == par1[b, k] and c != k]
+            assert int(tok1[b, k]) not in sib
+
+
+def test_topw_config4_rounds_on_device(ta):
+    """The draft-expansion workload's four rounds, each selected on the GPU
+    and checked against the oracle fed with the same tree and scores."""
+    import torch
+    c = config4_expand()
+    n_max = c.n_max
+    V = c.vocab
+    logits = np.zeros((1, n_max + 1, V), dtype=np.float32)
+    logits[0, 0] = c.logits_root
+    logits[0, 1:c.n0 + 1] = c.logits0
+    par = np.full((1, n_max), -1, dtype=np.int32)
+    tok = np.zeros((1, n_max), dtype=np.int32)
+    par[0, :c.n0] = c.parent0
+    tok[0, :c.n0] = c.tok0
+    cum = np.zeros((1, n_max), dtype=np.float32)
+    cum[0, :c.n0] = oracle.cumulative_scores(c.parent0, c.tok0, c.logits_root, c.logits0, c.n0)
+    d_lg = dev_tensor(logits)
+    d_par, d_tok, d_cum = dev_tensor(par), dev_tensor(tok), dev_tensor(cum)
+    d_n = dev_tensor(np.array([c.n0], np.int32))
+    n = c.n0
+    for r in range(c.rounds):
+        before = (d_par.cpu().numpy()[0].copy(), d_tok.cpu().numpy()[0].copy(),
+                  d_cum.cpu().numpy()[0].copy())
+        ta.tree_expand_top_w(d_lg, d_par, d_tok, d_cum, d_n, c.w)
+        torch.cuda.synchronize()
+        n1 = int(d_n.cpu().numpy()[0])
+        _check_round(before[0], before[1], before[2], n, logits[0], c.w, n_max,
+                     d_par.cpu().numpy()[0], d_tok.cpu().numpy()[0], d_cum.cpu().numpy()[0], n1)
+        # the new leaves' own distributions for the next round
+        logits[0, n + 1:n1 + 1] = c.logits_new[r]
+        d_lg.copy_(dev_tensor(logits))
+        n = n1
+    assert n == c.n0 + c.w * c.rounds

@@ -8,6 +8,7 @@ entry points keep the C names:
 * ``tree_attn_expand``   -- the same for the w newest leaves (non-square mask)
 * ``accept_greedy_path`` -- greedy longest accepted path, AL and bonus token
 * ``tree_cache_reroot``  -- evolving-tree-cache re-root with in-place KV moves
+* ``tree_expand_top_w``  -- maximum-likelihood expansion: append the w best leaves
 """
 from ._lib import (  # noqa: F401
     EXPORTED_SYMBOLS,
@@ -26,6 +27,8 @@ from ._lib import (  # noqa: F401
     tree_attn_verify,
     tree_attn_workspace_bytes,
     tree_cache_reroot,
+    tree_expand_top_w,
+    tree_expand_top_w_workspace_bytes,
 )
 
 __version__ = "0.1.0"

@@ -32,6 +32,8 @@ EXPORTED_SYMBOLS = (
     "tree_attn_expand",
     "accept_greedy_path",
     "tree_cache_reroot",
+    "tree_expand_top_w",
+    "tree_expand_top_w_workspace_bytes",
     "ta_status_string",
     "ta_version",
     "ta_last_error",
@@ -96,6 +98,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.tree_cache_reroot.argtypes = [ctypes.POINTER(ta_kv), c_int, vp, vp, vp, vp, vp, vp,
                                           c_int, c_int, c_int, c_int, c_int, vp]
         lib.tree_cache_reroot.restype = c_int
+        lib.tree_expand_top_w.argtypes = [vp, c_int, vp, vp, vp, vp, c_int, c_int, c_int, c_int,
+                                          vp, c_size, vp]
+        lib.tree_expand_top_w.restype = c_int
+        lib.tree_expand_top_w_workspace_bytes.argtypes = [c_int, c_int, c_int]
+        lib.tree_expand_top_w_workspace_bytes.restype = c_size
         lib.ta_status_string.argtypes = [c_int]
         lib.ta_status_string.restype = ctypes.c_char_p
         lib.ta_version.argtypes = []
@@ -392,3 +399,49 @@ def tree_cache_reroot(kv_layers: Sequence[KVCache], prefix_len, parent, n_nodes,
                                n_nodes.data_ptr(), path.data_ptr(), path_len.data_ptr(),
                                keep_subtree.data_ptr(), B, n_max, Hkv, d, dt, _stream(stream))
     _check(st)
+
+
+def tree_expand_top_w_workspace_bytes(B: int, n_max: int, w: int) -> int:
+    n = load_library().tree_expand_top_w_workspace_bytes(B, n_max, w)
+    if n == ctypes.c_size_t(-1).value:
+        raise TreeAttnError(TA_ERR_INVALID_ARG, "invalid sizes for a top-w workspace query")
+    return int(n)
+
+
+def tree_expand_top_w(logits, parent, tok, cum, n_nodes, w: int, workspace=None, stream=None):
+    """Append the ``w`` best new leaves (in place: parent, tok, cum, n_nodes).
+
+    ``logits`` is ``[B][n_max + 1][V]`` (row 0: after the root, row 1 + i:
+    after node i), fp32 or bf16; ``cum`` is the fp32 cumulative score of each
+    node.  Returns ``n_nodes``.
+    """
+    torch = _torch()
+    lib = load_library()
+    _need(logits, "logits", ndim=3)
+    dev = logits.device
+    _need(parent, "parent", dtype=torch.int32, ndim=2, device=dev)
+    _need(tok, "tok", dtype=torch.int32, ndim=2, device=dev)
+    _need(cum, "cum", dtype=torch.float32, ndim=2, device=dev)
+    _need(n_nodes, "n_nodes", dtype=torch.int32, ndim=1, device=dev)
+    B, rows, V = (int(x) for x in logits.shape)
+    n_max = int(parent.shape[1])
+    if rows != n_max + 1:
+        raise ValueError("logits must be [B][n_max + 1][V]")
+    for t, name in ((parent, "parent"), (tok, "tok"), (cum, "cum")):
+        if tuple(t.shape) != (B, n_max):
+            raise ValueError(f"{name} must be [B][n_max]")
+    if n_nodes.shape[0] != B:
+        raise ValueError("n_nodes must be [B]")
+    nbytes = tree_expand_top_w_workspace_bytes(B, n_max, int(w))
+    if workspace is None:
+        ws = _workspace_for(dev, nbytes)
+    else:
+        ws = workspace.get(nbytes, dev) if isinstance(workspace, Workspace) else workspace
+    if ws is not None:
+        _need(ws, "workspace", device=dev)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = lib.tree_expand_top_w(logits.data_ptr(), _dtype_code(logits), parent.data_ptr(),
+                               tok.data_ptr(), cum.data_ptr(), n_nodes.data_ptr(), B, n_max, V,
+                               int(w), _ptr(ws), ws_bytes, _stream(stream))
+    _check(st)
+    return n_nodes

@@ -294,6 +294,30 @@ int tree_cache_reroot(const ta_kv* kv_layers, int n_layers, int32_t* prefix_len,
   return hip_status(e, "tree_cache_reroot metadata launch");
 }
 
+size_t tree_expand_top_w_workspace_bytes(int B, int n_max, int w) {
+  if (B < 0 || n_max < 1 || n_max > TA_MAX_NODES || w < 1 || w > ta::kTopwMaxW)
+    return static_cast<size_t>(-1);
+  return ta::topw_ws_bytes(B, n_max, w);
+}
+
+int tree_expand_top_w(const void* logits, int logit_dtype, int32_t* parent, int32_t* tok,
+                      float* cum, int32_t* n_nodes, int B, int n_max, int V, int w, void* ws,
+                      size_t ws_bytes, void* stream) {
+  if (B < 0 || n_max < 1 || V < 1 || w < 1) return TA_ERR_INVALID_ARG;
+  if (n_max > TA_MAX_NODES) return TA_ERR_TREE_TOO_LARGE;
+  if (w > ta::kTopwMaxW || V > ta::kTopwMaxVocab) return TA_ERR_UNSUPPORTED;
+  if (logit_dtype != TA_F32 && logit_dtype != TA_BF16) return TA_ERR_UNSUPPORTED;
+  if (logits == nullptr || parent == nullptr || tok == nullptr || cum == nullptr ||
+      n_nodes == nullptr)
+    return TA_ERR_INVALID_ARG;
+  if (B == 0) return TA_OK;
+  if (ws == nullptr || ws_bytes < ta::topw_ws_bytes(B, n_max, w) || !aligned16(ws))
+    return TA_ERR_WORKSPACE;
+  hipError_t e = ta::launch_topw(logits, logit_dtype, parent, tok, cum, n_nodes, B, n_max, V, w,
+                                 ws, static_cast<hipStream_t>(stream));
+  return hip_status(e, "tree_expand_top_w launch");
+}
+
 const char* ta_status_string(int status) {
   switch (status) {
     case TA_OK: return "TA_OK";

@@ -80,6 +80,15 @@ hipError_t launch_accept(const void* logits, int logit_dtype, const int32_t* par
                          int B, int n_max, int V, int32_t* path, int32_t* path_len,
                          int32_t* bonus, hipStream_t s);
 
+// Top-w expansion: a rows pass (per-row log-sum-exp and w best allowed
+// tokens) then a select pass that appends the w best candidates.
+constexpr int kTopwMaxW = 16;
+constexpr int kTopwMaxVocab = 1 << 18;
+size_t topw_ws_bytes(int B, int n_max, int w);
+hipError_t launch_topw(const void* logits, int logit_dtype, int32_t* parent, int32_t* tok,
+                       float* cum, int32_t* n_nodes, int B, int n_max, int V, int w, void* ws,
+                       hipStream_t s);
+
 // Re-root: one launch per group of layers moves rows, then one updates metadata.
 constexpr int kRerootMaxLayersPerLaunch = 32;
 struct RerootLayer {
