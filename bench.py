@@ -27,9 +27,10 @@ Other workloads (``--workload``), each printing the same kind of line:
                      trees; step s reads KV copy s mod 16 (16 layers' worth,
                      538 MB), so no step finds its KV in the Infinity Cache.
   draft_expand       batch 1, Hq=32, Hkv=8, d=128, prefix 2048, a 64-node tree
-                     grown by 4 rounds of 8 new leaves (seeded random parents);
-                     one step = the 4 tree_attn_expand calls, on KV copy
-                     s mod 64 (563 MB in all).
+                     grown by 4 rounds of 8 new leaves; each round selects the
+                     leaves on the device (tree_expand_top_w over the root's
+                     and every node's 32000-way distribution) and attends them
+                     (tree_attn_expand), on KV copy s mod 64 (563 MB in all).
 
 Prints one JSON line (metric, value = microseconds per step, roofline of the
 attention call, CPU-oracle baseline on a bounded sample).
@@ -330,11 +331,15 @@ class TreeVerifyL70b(_Workload):
 
 
 class DraftExpand(_Workload):
-    """Four expansion rounds of w = 8 leaves over a 64-node tree.  Which
-    existing node each new leaf hangs under is drawn at random (seeded): the
-    attention cost does not depend on it, and choosing leaves is not part of
-    the timed path."""
-    phases = ("expand",)
+    """Four expansion rounds over a 64-node draft tree, all on the device: each
+    round tree_expand_top_w appends the w = 8 best leaves (maximum-likelihood
+    expansion over the 32000-way rows of the root and every node), then
+    tree_attn_expand attends the new leaves over prefix + tree.  The tree is
+    restored after the step (one elementwise kernel), so every step grows the
+    same tree.  Phases (HIP-graph mode): "expand" = the 4 attention calls, on
+    the trees the rounds produce; "topw" = one restore + the 4 selections.
+    With --eager the phases are not separated (the whole step is "expand")."""
+    phases = ("expand", "topw")
     COPIES = 64
 
     def __init__(self, ta, up):
@@ -342,61 +347,152 @@ class DraftExpand(_Workload):
         import torch
         from gen import config4_expand
         e = self.e = config4_expand()
-        self.ta = ta
+        self.ta, self.torch = ta, torch
         k, v = up(e.k, True), up(e.v, True)
         self.kvs = [ta.KVCache(k.clone(), v.clone()) for _ in range(self.COPIES)]
         del k, v
-        rng = np.random.default_rng([4, 999])
-        par = np.full((1, e.n_max), -1, dtype=np.int32)
-        par[0, : e.n0] = e.parent0
-        self.rounds = []
-        n = e.n0
+        nm = e.n_max
+        # draft distributions: row 0 after the root, row 1 + i after node i (the
+        # new leaves' rows are drawn up front; a round only reads existing nodes)
+        lg = np.zeros((1, nm + 1, e.vocab), dtype=np.float32)
+        lg[0, 0] = e.logits_root
+        lg[0, 1:e.n0 + 1] = e.logits0
         for r in range(e.rounds):
-            par[0, n: n + e.w] = rng.integers(0, n, size=e.w)
-            n += e.w
-            self.rounds.append((up(par.copy()), up(np.array([n], np.int32)),
-                                up(e.q_new[r], True)))
+            lg[0, e.n0 + 1 + r * e.w:e.n0 + 1 + (r + 1) * e.w] = e.logits_new[r]
+        self.logits = up(lg)
+        # tree state in one int32 buffer (parent, tok, cum bits, n) so that one
+        # kernel restores it
+        par = np.full(nm, -1, dtype=np.int32)
+        tok = np.zeros(nm, dtype=np.int32)
+        cum = np.zeros(nm, dtype=np.float32)
+        par[:e.n0], tok[:e.n0] = e.parent0, e.tok0
+        cum[:e.n0] = self._cum0(e)
+        meta = np.concatenate([par, tok, cum.view(np.int32), np.array([e.n0], np.int32)])
+        self.meta0 = up(meta)
+        self.meta = self.meta0.clone()
+        self.par = self.meta[0:nm].view(1, nm)
+        self.tok = self.meta[nm:2 * nm].view(1, nm)
+        self.cum = self.meta[2 * nm:3 * nm].view(torch.float32).view(1, nm)
+        self.n = self.meta[3 * nm:3 * nm + 1]
         self.P = up(np.array([e.P], np.int32))
-        self.outs = [torch.empty_like(q) for _, _, q in self.rounds]
+        self.qs = [up(e.q_new[r], True) for r in range(e.rounds)]
+        self.outs = [torch.empty_like(q) for q in self.qs]
         self.lses = [torch.empty((1, e.Hq, e.w), dtype=torch.float32, device=up.dev)
-                     for _ in self.rounds]
+                     for _ in self.qs]
+        self.snaps = None   # per-round (parent, n) after its selection, for the expand phase
+        self.topw_ws = ta.Workspace(up.dev)
         b = [attn_bytes([e.P], [e.n0 + e.w * (r + 1)], [e.w], e.Hq, e.Hkv, e.d)
              for r in range(e.rounds)]
         self.bytes = {key: sum(x[key] for x in b) for key in b[0]}
         self.config = {"workload": "draft_expand", "batch": 1, "Hq": e.Hq, "Hkv": e.Hkv,
                        "head_dim": e.d, "prefix": e.P, "tree_nodes": f"{e.n0}->{e.n_max}",
-                       "w": e.w, "rounds": e.rounds, "kv_copies": self.COPIES,
-                       "step": "4 expansion attention calls (one per round)"}
+                       "w": e.w, "rounds": e.rounds, "vocab": e.vocab, "kv_copies": self.COPIES,
+                       "step": "4 rounds of top-w selection + expansion attention (+ tree restore)"}
+
+    @staticmethod
+    def _cum0(e):
+        """Cumulative scores of the initial tree (fp32 of the fp64 sums), the
+        caller-kept state the selection extends."""
+        import numpy as np
+        lsm_root = e.logits_root.astype(np.float64)
+        lsm_root = lsm_root - (lsm_root.max() + np.log(np.exp(lsm_root - lsm_root.max()).sum()))
+        cum = np.zeros(e.n0, dtype=np.float64)
+        for i in range(e.n0):
+            p = int(e.parent0[i])
+            if p < 0:
+                cum[i] = lsm_root[int(e.tok0[i])]
+            else:
+                row = e.logits0[p].astype(np.float64)
+                lsm = row - (row.max() + np.log(np.exp(row - row.max()).sum()))
+                cum[i] = cum[p] + lsm[int(e.tok0[i])]
+        return cum.astype(np.float32)
+
+    def _round(self, r, kv, ws, opts):
+        self.ta.tree_expand_top_w(self.logits, self.par, self.tok, self.cum, self.n, self.e.w,
+                                  workspace=self.topw_ws)
+        self.ta.tree_attn_expand(self.qs[r], kv, self.P, self.par, self.n, self.e.scale,
+                                 out=self.outs[r], lse=self.lses[r], workspace=ws, **opts)
+
+    def _restore(self):
+        self.torch.add(self.meta0, 0, out=self.meta)
+
+    def step(self, i, ws, marks, opts):
+        kv = self.kvs[i % self.COPIES]
+        if marks is not None:
+            marks[0].record()
+        for r in range(self.e.rounds):
+            self._round(r, kv, ws, opts)
+        self._restore()
+        if marks is not None:
+            marks[1].record()
+            marks[2].record()
+
+    def _snapshots(self, ws, opts):
+        """Each round's tree after its selection (from one eager pass)."""
+        torch = self.torch
+        self._restore()
+        snaps = []
+        for r in range(self.e.rounds):
+            self.ta.tree_expand_top_w(self.logits, self.par, self.tok, self.cum, self.n,
+                                      self.e.w, workspace=self.topw_ws)
+            snaps.append((self.par.clone(), self.n.clone()))
+        self._restore()
+        torch.cuda.synchronize()
+        return snaps
 
     def phase(self, i, j, ws, opts):
+        if self.snaps is None:
+            raise RuntimeError("draft_expand phases need check() (after warm-up) first")
         kv = self.kvs[i % self.COPIES]
-        for r, (par, n, q) in enumerate(self.rounds):
-            self.ta.tree_attn_expand(q, kv, self.P, par, n, self.e.scale, out=self.outs[r],
-                                     lse=self.lses[r], workspace=ws, **opts)
+        if j == 0:
+            for r, (par, n) in enumerate(self.snaps):
+                self.ta.tree_attn_expand(self.qs[r], kv, self.P, par, n, self.e.scale,
+                                         out=self.outs[r], lse=self.lses[r], workspace=ws, **opts)
+        else:
+            self._restore()
+            for r in range(self.e.rounds):
+                self.ta.tree_expand_top_w(self.logits, self.par, self.tok, self.cum, self.n,
+                                          self.e.w, workspace=self.topw_ws)
 
     def attn_bytes(self, i):
         return self.bytes
 
     def check(self):
-        import torch
+        torch = self.torch
         for o, l in zip(self.outs, self.lses):
             if not (torch.isfinite(o.float()).all() and torch.isfinite(l).all()):
                 raise RuntimeError("non-finite expansion output")
+        if self.snaps is None:
+            self.snaps = self._snapshots(None, None)
+        e = self.e
+        if int(self.snaps[-1][1].item()) != e.n0 + e.w * e.rounds:
+            raise RuntimeError("the expansion rounds did not grow the tree to its full size")
 
     def cpu_baseline(self, budget):
+        """The oracle for one step: per round, top-w selection (fp64) and the
+        expansion attention of the new leaves."""
         import numpy as np
 
         import oracle
         e = self.e
+        par = np.full(e.n_max, -1, dtype=np.int32)
+        tok = np.zeros(e.n_max, dtype=np.int32)
+        par[:e.n0], tok[:e.n0] = e.parent0, e.tok0
+        rows = e.logits0.copy()
+        n = e.n0
         t0 = time.perf_counter()
-        for r, (par, n, _) in enumerate(self.rounds):
-            oc = copy.copy(self.c_like())
-            oc.parent = par.cpu().numpy()
-            oc.n_nodes = n.cpu().numpy()
+        for r in range(e.rounds):
+            cum = oracle.cumulative_scores(par, tok, e.logits_root, rows, n)
+            p, t, _ = oracle.select_top_w(par, tok, cum, e.logits_root, rows, n, e.w)
+            par[n:n + e.w], tok[n:n + e.w] = p, t
+            n += e.w
+            oc = self.c_like()
+            oc.parent, oc.n_nodes = par[None].copy(), np.array([n])
             oracle.expand(oc, e.q_new[r], e.w)
+            rows = np.concatenate([rows, e.logits_new[r]])
         dt = time.perf_counter() - t0
         return {"value": dt * 1e6, "unit": "us/step", "cores": _blas_threads(), "kind": "oracle",
-                "sample": "all 4 expansion rounds of one step (no sampling)",
+                "sample": "all 4 rounds of one step (top-w selection + expansion attention)",
                 "host_cpus": len(os.sched_getaffinity(0))}
 
     def c_like(self):
