@@ -8,8 +8,9 @@ root down to it; an expansion step takes the ``w`` best new leaves.
 Readings: the candidate pool is every (expanded node, token) pair whose token
 is not already a child of that node; the root (index -1) is expandable with
 its own logits row; ties break by higher score, then lower parent index,
-then lower token id.  The GPU library does not implement this step; it is
-the host-side driver of the expansion workload.
+then lower token id.  The library's tree_expand_top_w is checked against
+select_top_w; the draft-expansion workload's timing baseline calls both
+functions here once per round.
 """
 import numpy as np
 

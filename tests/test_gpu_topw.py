@@ -44,7 +44,9 @@ def _fp64_scores(parent, tok, cum, logits, n):
 
 def _check_round(par0, tok0, cum0, n0, logits, w, n_max, par1, tok1, cum1, n1):
     """One sequence's expansion step: GPU result (…1) against the oracle."""
-    take = min(w, n_max - n0)
+    avail = sum(int(logits.shape[1]) - sum(1 for c in range(n0) if int(par0[c]) == p)
+                for p in range(-1, n0))   # candidates that exist at all
+    take = min(w, n_max - n0, avail)
     assert n1 == n0 + take
     # existing nodes untouched
     np.testing.assert_array_equal(par1[:n0], par0[:n0])
@@ -166,3 +168,78 @@ def test_topw_config4_rounds_on_device(ta):
         d_lg.copy_(dev_tensor(logits))
         n = n1
     assert n == c.n0 + c.w * c.rounds
+
+
+def _single_tree(n, V, seed):
+    rng = np.random.default_rng([seed, 11])
+    parent = np.array([rng.integers(-1, i) for i in range(n)], dtype=np.int32)
+    tok = rng.integers(0, V, size=n).astype(np.int32)
+    # siblings take distinct tokens
+    for i in range(n):
+        while any(int(parent[c]) == int(parent[i]) and int(tok[c]) == int(tok[i]) for c in range(i)):
+            tok[i] = (tok[i] + 1) % V
+    return parent, tok
+
+
+@pytest.mark.parametrize("V,dtype", [(1 << 18, "f32"), (1 << 18, "bf16"), (40000, "f32"),
+                                     (70001, "bf16")])
+def test_topw_large_vocab(ta, V, dtype):
+    """Vocabularies past one load batch per thread (rows read in several
+    batches, the winners' logits read again), aligned and unaligned."""
+    n_max, n = 6, 3
+    parent, tok = _single_tree(n, V, 5)
+    par = np.full((1, n_max), -1, np.int32)
+    tk = np.zeros((1, n_max), np.int32)
+    par[0, :n], tk[0, :n] = parent, tok
+    logits = np.random.default_rng([V, 3]).standard_normal((1, n_max + 1, V), dtype=np.float32)
+    lg = logits[0].astype(np.float64)
+    if dtype == "bf16":
+        import torch
+        lg = torch.from_numpy(logits[0]).to(torch.bfloat16).float().numpy().astype(np.float64)
+    cum = np.zeros((1, n_max), np.float32)
+    cum[0, :n] = oracle.cumulative_scores(parent, tok, lg[0], lg[1:], n)
+    par1, tok1, cum1, n1, lg_used = _run(ta, logits, par, tk, cum, np.array([n], np.int32), 3, dtype)
+    _check_round(par[0], tk[0], cum[0], n, lg_used[0], 3, n_max, par1[0], tok1[0], cum1[0], int(n1[0]))
+
+
+@pytest.mark.parametrize("V,w,dtype", [(1000, 8, "f32"), (4096, 16, "bf16"), (777, 5, "f32")])
+def test_topw_all_ties(ta, V, w, dtype):
+    """Every logit equal: every thread's best logit ties, so the threshold
+    step ranks hundreds of keys; the picks are the root's lowest free tokens
+    in token order (equal scores: lower parent, then lower token)."""
+    n_max, n = 30, 6
+    parent = np.array([-1, -1, 0, 0, 1, -1] + [-1] * (n_max - 6), np.int32)[None]
+    tok = np.array([0, 2, 0, 1, 5, 3] + [0] * (n_max - 6), np.int32)[None]
+    logits = np.zeros((1, n_max + 1, V), np.float32)
+    cum = np.zeros((1, n_max), np.float32)
+    cum[0, :n] = oracle.cumulative_scores(parent[0], tok[0], logits[0, 0].astype(np.float64),
+                                          logits[0, 1:].astype(np.float64), n)
+    par1, tok1, cum1, n1, _ = _run(ta, logits, parent, tok, cum, np.array([n], np.int32), w, dtype)
+    assert int(n1[0]) == n + w
+    free_root = [t for t in range(V) if t not in (0, 2, 3)][:w]
+    assert par1[0, n:n + w].tolist() == [-1] * w
+    assert tok1[0, n:n + w].tolist() == free_root
+    np.testing.assert_allclose(cum1[0, n:n + w], -np.log(V), rtol=1e-6)
+
+
+def test_topw_inf_logits_and_scarce_tokens(ta):
+    """-inf logits score -inf but stay candidates; with fewer candidates in
+    the whole tree than w, all of them are appended, best first."""
+    V, n_max, n, w = 3, 10, 2, 8
+    parent = np.array([[-1, 0] + [-1] * (n_max - 2)], np.int32)
+    tok = np.array([[1, 2] + [0] * (n_max - 2)], np.int32)
+    logits = np.array([[[0.5, 2.0, -np.inf], [1.0, -np.inf, 3.0], [0.0, -1.0, -2.0]]
+                       + [[0.0, 0.0, 0.0]] * (n_max - 2)], np.float32)
+    cum = np.zeros((1, n_max), np.float32)
+    cum[0, :n] = oracle.cumulative_scores(parent[0], tok[0], logits[0, 0].astype(np.float64),
+                                          logits[0, 1:].astype(np.float64), n)
+    par1, tok1, cum1, n1, lg = _run(ta, logits, parent, tok, cum, np.array([n], np.int32), w)
+    # candidates: root {0, 2}, node 0 {0, 1}, node 1 {0, 1, 2}: 7 in all
+    assert int(n1[0]) == n + 7
+    P, T, S = oracle.select_top_w(parent[0], tok[0], cum[0].astype(np.float64), lg[0, 0], lg[0, 1:],
+                                  n, 7)
+    assert par1[0, n:n + 7].tolist() == P.tolist()
+    assert tok1[0, n:n + 7].tolist() == T.tolist()
+    fin = np.isfinite(S)
+    np.testing.assert_allclose(cum1[0, n:n + 7][fin], S[fin], rtol=1e-5, atol=2e-4)
+    assert np.all(np.isneginf(cum1[0, n:n + 7][~fin]))
