@@ -84,21 +84,27 @@ typedef struct {
 /* Optional tuning/testing knobs for the attention calls (NULL = automatic). */
 typedef struct {
   int32_t chunk_tokens;  /* KV tokens per split-KV work item, a multiple of 64; 0 = auto */
-  int32_t kernel;        /* 0 = auto (3 for bf16, else 1); 1 = generic fp32-math kernel;
+  int32_t kernel;        /* 0 = auto (bf16: 4 for paged caches, 3 for contiguous ones;
+                            else 1); 1 = generic fp32-math kernel;
                             2 = bf16 MFMA kernel, register prefetch; 3 = bf16 MFMA kernel,
                             LDS-DMA ring and pipelined tiles (paged calls whose split spans
-                            more than 510 blocks run on kernel 2) */
+                            more than 510 blocks run on kernel 2); 4 = bf16 MFMA kernel over
+                            balanced units: every job's KV tiles end to end, one equal range
+                            per resident work group, the ring running across jobs (B <= 1024;
+                            chunk_tokens is ignored) */
 } ta_attn_opts;
 
 /*
  * Workspace (bytes) needed by tree_attn_verify / tree_attn_expand for these
- * sizes.  n_q is n_max for verify and w for expand.  The workspace holds the
- * split-KV partial results (per split and query row: running maximum, sum and
- * unnormalised output) that a second, combining launch of the same call
- * reads; its contents need no initialisation and are meaningless between
- * calls.  Calls that overlap in time must not share a workspace.  Returns 0
- * when no split is needed (ws may then be NULL), or (size_t)-1 for invalid
- * sizes.
+ * sizes, enough for the plan of a contiguous and of a paged cache alike.
+ * n_q is n_max for verify and w for expand.  The workspace holds the split-KV
+ * partial results (per split or work-group range and query row: running
+ * maximum, sum and unnormalised output) that a second, combining launch of
+ * the same call reads, and for kernel 4 its table of stream starts; its
+ * contents need no initialisation and are meaningless between calls.  Calls
+ * that overlap in time must not share a workspace.  Returns 0 when the plans
+ * need none (kernels 1-3 without a split; ws may then be NULL), or
+ * (size_t)-1 for invalid sizes.
  */
 size_t tree_attn_workspace_bytes(int B, int n_q, int Hq, int Hkv, int d, int dtype, int T_cap,
                                  const ta_attn_opts* opts);

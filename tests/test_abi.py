@@ -58,10 +58,19 @@ def test_invalid_arguments_are_rejected_on_the_host():
     assert _verify(lib, kv=_lib.ta_kv(0x1000, 0x2000, 0x3000, 16, 4, 8, 65)) == \
         _lib.TA_ERR_INVALID_ARG
     assert _verify(lib, B=0) == _lib.TA_OK                        # nothing to do
-    # a plan that splits needs a workspace
-    need = ta.tree_attn_workspace_bytes(1, 16, 8, 2, 128, ta.TA_BF16, 64, chunk_tokens=64)
+    # a split-kernel plan that does not split needs no workspace; the units
+    # kernel (automatic for paged bf16 caches, so part of the layout-independent
+    # answer) always needs one: its stream table and two partial slots per group
+    need = ta.tree_attn_workspace_bytes(1, 16, 8, 2, 128, ta.TA_BF16, 64, chunk_tokens=64,
+                                        kernel=3)
     assert need == 0
-    need = ta.tree_attn_workspace_bytes(2, 16, 8, 2, 128, ta.TA_BF16, 4096, chunk_tokens=256)
+    units = ta.tree_attn_workspace_bytes(1, 16, 8, 2, 128, ta.TA_BF16, 64, kernel=4)
+    assert units > 0
+    assert ta.tree_attn_workspace_bytes(1, 16, 8, 2, 128, ta.TA_BF16, 64) >= units
+    # (kernel 3 for both layouts: the query then sizes exactly the plan the
+    # contiguous call below runs)
+    need = ta.tree_attn_workspace_bytes(2, 16, 8, 2, 128, ta.TA_BF16, 4096, chunk_tokens=256,
+                                        kernel=3)
     assert need > 0
     opts = _lib.ta_attn_opts(256, 0)
     st = lib.tree_attn_verify(0x4000, _kv(4096), 0x5000, 0x6000, 0x7000, 2, 16, 8, 2, 128,

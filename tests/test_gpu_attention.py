@@ -95,7 +95,7 @@ BOTH_KERNELS = [
 
 
 @pytest.mark.parametrize("case", BOTH_KERNELS, ids=[f"seed{c[0]}" for c in BOTH_KERNELS])
-@pytest.mark.parametrize("kernel", [1, 2, 3])
+@pytest.mark.parametrize("kernel", [1, 2, 3, 4])
 def test_bf16_both_kernels(ta, case, kernel):
     seed, B, Hq, Hkv, d, P_range, n_max, target_side, paged, chunk = case
     c = random_case(seed, B, Hq, Hkv, d, P_range=P_range, n_max=n_max, dtype="bf16",
@@ -126,6 +126,38 @@ def test_random_expand(ta, w):
     Or, Lr = oracle.expand(c, qe_np, w)
     assert_attn_close(O, L, Or, Lr, "bf16", what=f"expand w={w}")
     _check_unwritten(O, L, c, lambda n: [n - w + r for r in range(w)])
+
+
+@pytest.mark.parametrize("w", [1, 8])
+def test_units_kernel_expand(ta, w):
+    """Expansion rows through the units kernel (kernel 4)."""
+    import torch
+    c = random_case(60 + w, 5, 32, 8, 128, P_range=(0, 1500), n_max=24, n_range=(1, 24),
+                    dtype="bf16", paged=True)
+    dc = DevCase(c)
+    qe = dc.q[:, :w].contiguous()
+    out = torch.full_like(qe, float("nan"))
+    lse = torch.full((c.B, c.Hq, w), float("nan"), dtype=torch.float32, device=qe.device)
+    ta.tree_attn_expand(qe, dc.kv, dc.prefix_len, dc.parent, dc.n_nodes, c.scale, out=out,
+                        lse=lse, kernel=4)
+    torch.cuda.synchronize()
+    O, L = to_f64(out), lse.cpu().numpy()
+    Or, Lr = oracle.expand(c, c.q[:, :w], w)
+    assert_attn_close(O, L, Or, Lr, "bf16", what=f"units expand w={w}")
+    _check_unwritten(O, L, c, lambda n: [n - w + r for r in range(w)])
+
+
+@pytest.mark.parametrize("seed", [90, 91])
+def test_units_kernel_mixed_lengths(ta, seed):
+    """Paged batch with lengths from 0 to ~6000 (jobs of 1 to ~190 tiles):
+    ranges cut jobs at arbitrary tiles, some groups hold several whole jobs."""
+    c = random_case(seed, 12, 16, 4, 128, P_range=(0, 6000), n_max=10, dtype="bf16",
+                    target_side=seed == 91, paged=True)
+    dc = DevCase(c)
+    O, L = _run_verify(ta, dc, 0, 4)
+    Or, Lr = oracle.verify(c)
+    assert_attn_close(O, L, Or, Lr, "bf16", what=f"units mixed seed{seed}")
+    _check_unwritten(O, L, c, lambda n: range(c.n_max))
 
 
 def test_split_count_invariance(ta):

@@ -49,7 +49,8 @@ constexpr int kGenericRows = 32;
 constexpr int kMfmaRows = 128;  // query rows (G x nodes) per MFMA work group, at most
 
 struct Plan {
-  int kernel;         // 1 generic, 2 MFMA (register prefetch), 3 MFMA (LDS-DMA ring)
+  int kernel;         // 1 generic, 2 MFMA (register prefetch), 3 MFMA (LDS-DMA ring),
+                      // 4 MFMA over balanced units (LDS-DMA ring across jobs)
   int rows_per_tile;
   int n_row_tiles;
   int chunk;
@@ -69,10 +70,18 @@ bool make_plan(int B, int n_q, int Hq, int Hkv, int d, int dtype, int T_cap, boo
   const int R = n_q * G;
   int kernel = opts ? opts->kernel : 0;
   const bool mfma_ok = dtype == TA_BF16 && (d == 128 || d == 64);
-  // automatic: the streaming MFMA kernel for bf16, the generic kernel otherwise
-  if (kernel == 0) kernel = mfma_ok ? 3 : 1;
-  if ((kernel == 2 || kernel == 3) && !mfma_ok) return false;
-  if (kernel < 1 || kernel > 3) return false;
+  // Automatic: bf16 paged caches (the mixed-length serving layout) take the
+  // units kernel, which gives every work group the same number of KV tiles
+  // whatever the length mix; contiguous bf16 caches (one capacity, the
+  // equal-length case) the streaming kernel; anything else the generic one.
+  if (kernel == 0) {
+    const long long tiles_max = static_cast<long long>(B) * Hkv *
+                                ((n_q * G + kMfmaRows - 1) / kMfmaRows + 1) * ((T_cap + 31) / 32);
+    const bool units_ok = paged && B <= ta::kUnitMaxSeqs && tiles_max < (1LL << 31);
+    kernel = mfma_ok ? (units_ok ? 4 : 3) : 1;
+  }
+  if (kernel >= 2 && !mfma_ok) return false;
+  if (kernel < 1 || kernel > 4) return false;
   pl.kernel = kernel;
   // Both MFMA kernels share one plan (so they need the same workspace): tiles
   // hold 32 x NRG rows (NRG = 1..4 row groups of 32).
@@ -80,6 +89,19 @@ bool make_plan(int B, int n_q, int Hq, int Hkv, int d, int dtype, int T_cap, boo
   pl.rows_per_tile = mfma ? std::min(kMfmaRows, round_up(R, 32)) : kGenericRows;
   pl.n_row_tiles = (R + pl.rows_per_tile - 1) / pl.rows_per_tile;
   const long long items = static_cast<long long>(B) * Hkv * pl.n_row_tiles;
+  if (kernel == 4) {
+    // G work groups (two per compute unit, all resident) share the stream of
+    // at most items * ceil(T_cap / 32) tiles; the stream positions are int.
+    if (B > ta::kUnitMaxSeqs) return false;
+    if (items * ((T_cap + 31) / 32) >= (1LL << 31)) return false;
+    const int groups = 2 * device_cu_count();
+    pl.chunk = T_cap;
+    pl.n_split = groups;
+    const size_t slots = 2 * static_cast<size_t>(groups) * pl.rows_per_tile;
+    pl.ws_bytes = slots * d * sizeof(float) + slots * 2 * sizeof(float) +
+                  (static_cast<size_t>(B) + 1) * sizeof(int32_t);
+    return true;
+  }
   int chunk = opts ? opts->chunk_tokens : 0;
   if (chunk < 0 || chunk % 64 != 0) return false;
   if (chunk == 0) {
@@ -181,7 +203,13 @@ int run_attention(const void* q, ta_kv kv, const int32_t* prefix_len, const int3
   p.n_split = pl.n_split;
   p.rows_per_tile = pl.rows_per_tile;
   p.n_row_tiles = pl.n_row_tiles;
-  if (pl.ws_bytes > 0) {
+  if (pl.kernel == 4) {
+    const size_t slots = 2 * static_cast<size_t>(pl.n_split) * pl.rows_per_tile;
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    p.ws_o = reinterpret_cast<float*>(base);
+    p.ws_ml = reinterpret_cast<float*>(base + slots * d * sizeof(float));
+    p.ws_seq = reinterpret_cast<int32_t*>(base + slots * (d + 2) * sizeof(float));
+  } else if (pl.ws_bytes > 0) {
     const int tiles = B * Hkv * pl.n_row_tiles;
     const size_t parts = static_cast<size_t>(tiles) * pl.n_split * pl.rows_per_tile;
     uint8_t* base = static_cast<uint8_t*>(ws);
@@ -191,6 +219,15 @@ int run_attention(const void* q, ta_kv kv, const int32_t* prefix_len, const int3
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   const char* where;
+  if (pl.kernel == 4) {
+    e = ta::launch_attn_units(p, s);
+    where = "attention (units kernel) launch";
+    if (e == hipSuccess) {
+      e = ta::launch_attn_merge_units(p, s);
+      where = "attention units combine launch";
+    }
+    return hip_status(e, where);
+  }
   if (pl.kernel == 3) {
     e = ta::launch_attn_stream(p, 4, s);
     where = "attention (streaming MFMA kernel) launch";

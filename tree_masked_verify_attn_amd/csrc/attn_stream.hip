@@ -19,86 +19,10 @@
 //    ring loop issues no other vector-memory loads.
 //  * A split sequence leaves partial (max, sum, output) states in the
 //    workspace; the combine launch (attn_merge.hip) finishes it.
-#include "ta_device.h"
+#include "stream_common.h"
 
 namespace ta {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
-
-constexpr int kThreads = 256;
-constexpr int kTile = 32;             // KV positions per ring stage
-constexpr float kRescaleSlack = 8.f;  // log2 units
-constexpr float kLn2 = 0.69314718055994530942f;
-constexpr int kMaxSplitBlocks = 512;  // paged: block ids of one split cached in LDS
-
-template <int D>
-__device__ __forceinline__ int swz(int t) {
-  const int h = ((t & 3) << 1) | ((t >> 2) & 1);
-  return D == 128 ? (h | (((t >> 3) & 1) << 3)) : h;
-}
-template <int D>
-__device__ __forceinline__ int lds_off(int t, int chunk) {  // bytes within a K or V stage
-  return t * (D * 2) + ((chunk ^ swz<D>(t)) << 4);
-}
-
-__device__ __forceinline__ float lane_swap32(float x) {
-  const uint32_t u = __float_as_uint(x);
-  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return __uint_as_float((threadIdx.x & 63) < 32 ? r[1] : r[0]);
-}
-
-// 64 lanes x 16 bytes from `g` (per lane) into LDS [lds_base, lds_base + 1 KiB).
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :
-               : "s"(lds_base), "v"(g)
-               : "memory");
-}
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
-}
-// Workgroup barrier without the fence of __syncthreads (which would wait for
-// every outstanding load); the wave's own LDS reads are complete first.
-__device__ __forceinline__ void raw_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
-}
-
-template <int D, int NRG, int S>
-struct SCfg {
-  static constexpr int CH = D / 8;                  // 16-byte chunks per row
-  static constexpr int ROW = D * 2;                 // bytes per row
-  static constexpr int HALF = kTile * ROW;          // K (or V) bytes per stage
-  static constexpr int STAGE = 2 * HALF;
-  static constexpr int ROWS_PER_INST = 1024 / ROW;  // rows one 1 KiB load covers
-  static constexpr int INST_PER_WAVE = HALF / 1024 / 4;  // per wave, for K (same for V)
-  static constexpr int NL = 2 * INST_PER_WAVE;      // loads per thread per stage
-  static constexpr int KS = D / 16;
-  static constexpr int MB = D / 32;
-  static constexpr int RPT = 32 * NRG;
-  static constexpr int RING = S * STAGE;
-  static constexpr int SETUP = kMaxNodes * kMaskWords * 8 + kMaxNodes * 4;  // anc + jump
-  static constexpr int LDS = RING > SETUP ? RING : SETUP;
-};
-
-template <int N, int NL>
-__device__ __forceinline__ void wait_stage(int pending_after) {
-  // pending_after = stages issued after the one we need (0 .. N)
-  if constexpr (N >= 3) {
-    if (pending_after >= 3) { wait_vmcnt<3 * NL>(); return; }
-  }
-  if constexpr (N >= 2) {
-    if (pending_after >= 2) { wait_vmcnt<2 * NL>(); return; }
-  }
-  if (pending_after >= 1) { wait_vmcnt<NL>(); return; }
-  wait_vmcnt<0>();
-}
 
 // S = 4: 64 KiB ring, two work groups per compute unit.  S = 3: 48 KiB ring and
 // registers capped for three work groups per compute unit.

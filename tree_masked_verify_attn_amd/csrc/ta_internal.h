@@ -60,6 +60,10 @@ struct AttnParams {
   // workspace (only when n_split > 1)
   float* ws_o;          // [tiles][n_split][rows_per_tile][d] unnormalised partial outputs
   float* ws_ml;         // [tiles][n_split][rows_per_tile][2]  running max (log2) and sum
+  // units kernel only: n_split is its number of work groups G, ws_o / ws_ml
+  // hold 2G slots of rows_per_tile rows, ws_seq the stream start of every
+  // sequence and the stream's length (B + 1 entries)
+  int32_t* ws_seq;
 };
 
 // Workspace layout: the partial outputs, then the (max, sum) pairs.  Returns
@@ -73,6 +77,11 @@ hipError_t launch_attn_mfma(const AttnParams& p, hipStream_t s);
 // Streaming MFMA variant: `stages` (3 or 4) 32-position LDS stages in flight.
 hipError_t launch_attn_stream(const AttnParams& p, int stages, hipStream_t s);
 constexpr int kStreamMaxSplitBlocks = 512;  // paged: block ids of one split held in LDS
+// Units kernel: every (sequence, row tile, KV head) job's tiles laid end to end,
+// G equal ranges of them, one per work group; then a combine launch.
+constexpr int kUnitMaxSeqs = 1024;
+hipError_t launch_attn_units(const AttnParams& p, hipStream_t s);
+hipError_t launch_attn_merge_units(const AttnParams& p, hipStream_t s);
 
 // Accept: argmax pass (writes a[i] into path) then the path pass.
 hipError_t launch_accept(const void* logits, int logit_dtype, const int32_t* parent,
