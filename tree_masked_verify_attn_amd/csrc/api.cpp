@@ -76,7 +76,8 @@ bool make_plan(int B, int n_q, int Hq, int Hkv, int d, int dtype, int T_cap, boo
   // equal-length case) the streaming kernel; anything else the generic one.
   if (kernel == 0) {
     const long long tiles_max = static_cast<long long>(B) * Hkv *
-                                ((n_q * G + kMfmaRows - 1) / kMfmaRows + 1) * ((T_cap + 31) / 32);
+                                ((n_q * G + kMfmaRows - 1) / kMfmaRows + 1) *
+                                ((T_cap + 31) / 32 + ta::kUnitJobCost);
     const bool units_ok = paged && B <= ta::kUnitMaxSeqs && tiles_max < (1LL << 31);
     kernel = mfma_ok ? (units_ok ? 4 : 3) : 1;
   }
@@ -93,7 +94,7 @@ bool make_plan(int B, int n_q, int Hq, int Hkv, int d, int dtype, int T_cap, boo
     // G work groups (two per compute unit, all resident) share the stream of
     // at most items * ceil(T_cap / 32) tiles; the stream positions are int.
     if (B > ta::kUnitMaxSeqs) return false;
-    if (items * ((T_cap + 31) / 32) >= (1LL << 31)) return false;
+    if (items * ((T_cap + 31) / 32 + ta::kUnitJobCost) >= (1LL << 31)) return false;
     const int groups = 2 * device_cu_count();
     pl.chunk = T_cap;
     pl.n_split = groups;

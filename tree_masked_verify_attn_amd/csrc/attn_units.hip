@@ -7,9 +7,12 @@
 //  * The tiles (32 KV positions) of every job (sequence, row tile, KV head)
 //    are laid end to end in one stream: KV heads outermost, then sequences,
 //    then row tiles (so that the jobs of one short sequence do not crowd into
-//    one range).  With N tiles and G work groups, group g takes the
-//    contiguous range [g*U, (g+1)*U), U = ceil(N / G): every group streams
-//    the same number of tiles whatever the length mix, and all G groups are
+//    one range).  Each job also counts kJobCost tiles that are never loaded:
+//    what a job costs beyond its tiles (its mask set-up, the change of job,
+//    a partly filled last tile), so that a range of many short jobs holds
+//    fewer tiles.  With N such units and G work groups, group g takes the
+//    contiguous range [g*U, (g+1)*U), U = ceil(N / G): every group gets the
+//    same amount of work whatever the length mix, and all G groups are
 //    resident at once (two per compute unit).
 //  * A range holds pieces of one or more jobs ("segments").  The LDS-DMA ring
 //    runs across segment boundaries: the loads of the next segment's first
@@ -31,6 +34,7 @@ namespace ta {
 namespace {
 
 constexpr int kMaxSeg = 16;
+constexpr int kJobCost = kUnitJobCost;
 constexpr int kUnitBlocks = 512;
 // Row masks of the segments that reach a tree cache: as many as fit in 12 KiB.
 template <int RPT>
@@ -109,7 +113,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_units_kernel(AttnParams p) {
   __shared__ USeg sSeg[kMaxSeg];
   __shared__ uint64_t sRowMask[kMaxTreeSeg][RPT][kMaskWords];
   __shared__ int sScan[kThreads / 64];
-  __shared__ int sNumSeg, sBatchTiles;
+  __shared__ int sNumSeg, sBatchTiles, sNext;
 
   const int g = blockIdx.x;
   const int G = gridDim.x;
@@ -143,7 +147,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_units_kernel(AttnParams p) {
       cnt[k] = 0;
       if (b < B) {
         const SeqJobs s = seq_jobs(p, b, RPT);
-        cnt[k] = s.rts * s.tiles;
+        cnt[k] = s.tiles > 0 ? s.rts * (s.tiles + kJobCost) : 0;
         sTiles[b] = s.tiles;
         sRtlo[b] = s.rt_lo;
         sP[b] = s.P;
@@ -176,7 +180,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_units_kernel(AttnParams p) {
     return total;
   };
 
-  int Sh = load_stream();  // tiles per KV head
+  int Sh = load_stream();  // stream units per KV head
   if (g == 0) {  // the combine launch reads the stream starts
     for (int b = tid; b <= B; b += kThreads) p.ws_seq[b] = sS[b];
   }
@@ -227,9 +231,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_units_kernel(AttnParams p) {
         }
         while (b < B && sS[b + 1] <= xh) ++b;  // skip sequences with no tiles
         const int tiles = sTiles[b];
+        const int stride = tiles + kJobCost;  // a job's units in the stream
         const int off = xh - sS[b];
-        const int job = off / tiles;  // row tile within the sequence
-        const int jt = off - job * tiles;
+        const int job = off / stride;  // row tile within the sequence
+        const int jt = off - job * stride;
+        if (jt >= tiles) {  // the job's cost units: nothing to load
+          xs = min(x1, xs + stride - jt);
+          continue;
+        }
         int take = min(tiles - jt, x1 - xs);
         const int P = sP[b], n = sN[b], T = P + n;
         const int tb = jt * kTile;
@@ -270,15 +279,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_units_kernel(AttnParams p) {
         if (paged) nblk += (te - 1) / bs - tb / bs + 1;
         jl += take;
         xs += take;
+        if (jt + take == tiles) xs = min(x1, xs + kJobCost);  // past the job's cost units
         ++k;
       }
       sNumSeg = k;
       sBatchTiles = jl;
+      sNext = xs;
     }
     __syncthreads();
     const int nseg = sNumSeg;
     const int L = sBatchTiles;
-    x += L;
+    x = sNext;
+    if (nseg == 0) continue;  // uniform: the rest of the range held cost units only
     // Block ids (paged) and the parents of the segments that reach a tree
     // cache, in one round of loads (the sequence tables are done with).
     int* sPar = reinterpret_cast<int*>(sRing);  // [kMaxTreeSeg][kMaxNodes]
@@ -673,12 +685,12 @@ __global__ __launch_bounds__(kThreads) void merge_units_kernel(AttnParams p) {
   const int node = p.expand ? s.n - p.n_q + slot : slot;
   if (node < 0 || node >= s.n) return;
 
-  const int Sh = p.ws_seq[p.B];  // tiles per KV head
+  const int Sh = p.ws_seq[p.B];  // stream units per KV head
   const int N = Sh * p.Hkv;
   const int G = p.n_split;  // work groups of the attention launch
   const int U = (N + G - 1) / G;
-  const int J0 = hkv * Sh + p.ws_seq[b] + (rtile - s.rt_lo) * s.tiles;
-  const int J1 = J0 + s.tiles;
+  const int J0 = hkv * Sh + p.ws_seq[b] + (rtile - s.rt_lo) * (s.tiles + kJobCost);
+  const int J1 = J0 + s.tiles;  // the job's tiles (its cost units follow)
   const int g0 = J0 / U, g1 = (J1 - 1) / U;
   if (g0 == g1) return;  // one group held the whole job and wrote its rows
 
