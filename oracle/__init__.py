@@ -22,8 +22,10 @@ Modules:
 * ``attention`` -- explicit-mask softmax attention in float64.
 * ``accept``    -- greedy longest accepted path by enumerating every node.
 * ``reroot``    -- evolving-tree-cache re-root and KV compaction.
-* ``topw``      -- top-w maximum-likelihood candidate selection (host side of
-  the draft expansion rounds).
+* ``topw``      -- top-w maximum-likelihood candidate selection (the draft
+  expansion rounds).
+* ``draft``     -- the draft side's walk along the verified tokens and the
+  choice of the subtree to send (Algorithm 1, Re-root and Select).
 * ``bf16``      -- exact bfloat16 -> float64 decoding.
 
 Pins: every function here is checked in ``tests/test_oracle_*.py`` against
@@ -38,3 +40,4 @@ from .attention import tree_attention, verify, expand, gather_sequence_kv  # noq
 from .accept import accept_greedy_path, argmax_first  # noqa: F401
 from .reroot import tree_cache_reroot  # noqa: F401
 from .topw import cumulative_scores, select_top_w  # noqa: F401
+from .draft import token_walk, select_subtree  # noqa: F401
