@@ -219,6 +219,52 @@ int tree_expand_top_w(const void* logits, int logit_dtype, int32_t* parent, int3
 /* Workspace (bytes) for tree_expand_top_w, or (size_t)-1 for invalid sizes. */
 size_t tree_expand_top_w_workspace_bytes(int B, int n_max, int w);
 
+/*
+ * Draft-side walk along the target's verified tokens ([SS] Section 3.1.1
+ * Algorithm 1, Synchronize and Re-root; Section 3.2 update procedure;
+ * Section 3.1.2 Figure 2).
+ *
+ *   parent [B][n_max], tok [B][n_max], n_nodes [B]: the draft tree
+ *   verified [B][m_max] int32, verified_len [B] int32: the tokens the target
+ *            verified after the root, in order (the bonus token included)
+ *   path [B][n_max] int32 out, path_len [B] int32 out, keep [B] uint8 out
+ *
+ * From the root (parent -1), each verified token that is the token of a
+ * child of the current node moves the walk to that child (the lowest index
+ * among children with equal tokens); the walk stops at the first token that
+ * no child carries.  path gets the matched nodes, path_len their number, and
+ * keep = 1 when every verified token matched (the last one becomes the root
+ * and its subtree stays), else 0 (a new tree starts; the tokens after the
+ * match need the draft model).  The outputs are the path / path_len /
+ * keep_subtree arguments of tree_cache_reroot.  1 <= m_max <= 1024;
+ * verified_len is clamped to [0, m_max].  All pointers are device pointers.
+ */
+int tree_token_walk(const int32_t* parent, const int32_t* tok, const int32_t* n_nodes,
+                    const int32_t* verified, const int32_t* verified_len, int B, int n_max,
+                    int m_max, int32_t* path, int32_t* path_len, uint8_t* keep, void* stream);
+
+/*
+ * The subtree of bs nodes to send to the target ([SS] Section 3.1.1
+ * Algorithm 1, Select: the most promising subtree of size bs).
+ *
+ *   cum [B][n_max] fp32: cumulative log-probability of each node (as
+ *            tree_expand_top_w keeps it); parent, tok, n_nodes: the tree
+ *   sel_node, sel_parent, sel_tok [B][bs] int32 out; sel_n [B] int32 out
+ *
+ * The min(bs, n) nodes of largest cum (ties: lower index; NaN ranks last)
+ * are chosen.  When cum does not increase from a parent to its child (true of
+ * cumulative log-probabilities) they form a subtree and maximise the sum of
+ * exp(cum), the expected number of accepted tokens under the draft model.
+ * They are written in node order: sel_node the node index, sel_parent the
+ * position of its parent inside the selection (-1: child of the root; also
+ * for a parent that was not chosen, which only scores rising along a path
+ * cause), sel_tok its token; entries past sel_n[b] are -1 / -1 / 0.
+ * 1 <= bs <= n_max.  All pointers are device pointers.
+ */
+int tree_select_subtree(const float* cum, const int32_t* parent, const int32_t* tok,
+                        const int32_t* n_nodes, int B, int n_max, int bs, int32_t* sel_node,
+                        int32_t* sel_parent, int32_t* sel_tok, int32_t* sel_n, void* stream);
+
 /* Human-readable name of a ta_status value (static string). */
 const char* ta_status_string(int status);
 

@@ -25,7 +25,9 @@ Readings (the pages leave these open):
   child (log-probabilities are <= 0), so the bs nodes of largest cum, ties
   broken by lower index, form a subtree (every chosen node's parent comes
   before it in that order) and maximise the sum; ``select_subtree`` returns
-  them in node order with parents renumbered inside the selection.
+  them in node order with parents renumbered inside the selection.  For
+  scores that rise along a path (outside that contract) a chosen node whose
+  parent was left out gets parent -1.
 """
 import numpy as np
 
@@ -54,6 +56,7 @@ def select_subtree(parent, tok, cum, n: int, bs: int):
     order = sorted(range(n), key=lambda i: (-float(cum[i]), i))
     chosen = sorted(order[:min(bs, n)])
     pos = {v: k for k, v in enumerate(chosen)}
-    new_parent = [pos[int(parent[v])] if int(parent[v]) >= 0 else -1 for v in chosen]
+    # a parent left out (only scores that rise along a path do that) reads -1
+    new_parent = [pos.get(int(parent[v]), -1) if int(parent[v]) >= 0 else -1 for v in chosen]
     return (np.array(chosen, dtype=np.int32), np.array(new_parent, dtype=np.int32),
             np.array([int(tok[v]) for v in chosen], dtype=np.int32))

@@ -152,3 +152,36 @@ def test_binding_refuses_host_memory_for_device_arguments():
         _lib._need(torch.zeros(4), "workspace")
     with pytest.raises(ValueError):
         ta.KVCache(torch.zeros(1, 4, 1, 64), torch.zeros(1, 4, 1, 64))
+
+
+def test_draft_side_host_side_validation():
+    """tree_token_walk / tree_select_subtree reject bad sizes and null
+    pointers before any launch (no GPU needed for these paths)."""
+    lib = ensure_built()
+    P = 0x1000
+
+    def walk(B=2, n_max=16, m_max=8, ptrs=(P,) * 8):
+        return lib.tree_token_walk(*ptrs[:5], B, n_max, m_max, *ptrs[5:], None)
+
+    assert walk(B=0) == _lib.TA_OK
+    assert walk(B=-1) == _lib.TA_ERR_INVALID_ARG
+    assert walk(n_max=0) == _lib.TA_ERR_INVALID_ARG
+    assert walk(n_max=257) == _lib.TA_ERR_TREE_TOO_LARGE
+    assert walk(m_max=0) == _lib.TA_ERR_INVALID_ARG
+    assert walk(m_max=1025) == _lib.TA_ERR_UNSUPPORTED
+    for i in range(8):
+        ptrs = [P] * 8
+        ptrs[i] = None
+        assert walk(ptrs=tuple(ptrs)) == _lib.TA_ERR_INVALID_ARG, i
+
+    def select(B=2, n_max=16, bs=4, ptrs=(P,) * 8):
+        return lib.tree_select_subtree(*ptrs[:4], B, n_max, bs, *ptrs[4:], None)
+
+    assert select(B=0) == _lib.TA_OK
+    assert select(bs=0) == _lib.TA_ERR_INVALID_ARG
+    assert select(bs=17) == _lib.TA_ERR_INVALID_ARG
+    assert select(n_max=257, bs=4) == _lib.TA_ERR_TREE_TOO_LARGE
+    for i in range(8):
+        ptrs = [P] * 8
+        ptrs[i] = None
+        assert select(ptrs=tuple(ptrs)) == _lib.TA_ERR_INVALID_ARG, i

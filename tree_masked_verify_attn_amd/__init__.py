@@ -9,6 +9,8 @@ entry points keep the C names:
 * ``accept_greedy_path`` -- greedy longest accepted path, AL and bonus token
 * ``tree_cache_reroot``  -- evolving-tree-cache re-root with in-place KV moves
 * ``tree_expand_top_w``  -- maximum-likelihood expansion: append the w best leaves
+* ``tree_token_walk``    -- draft side: walk along the verified tokens (re-root path)
+* ``tree_select_subtree``-- draft side: the size-bs subtree to send
 """
 from ._lib import (  # noqa: F401
     EXPORTED_SYMBOLS,
@@ -29,6 +31,8 @@ from ._lib import (  # noqa: F401
     tree_cache_reroot,
     tree_expand_top_w,
     tree_expand_top_w_workspace_bytes,
+    tree_select_subtree,
+    tree_token_walk,
 )
 
 __version__ = "0.1.0"

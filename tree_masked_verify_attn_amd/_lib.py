@@ -34,6 +34,8 @@ EXPORTED_SYMBOLS = (
     "tree_cache_reroot",
     "tree_expand_top_w",
     "tree_expand_top_w_workspace_bytes",
+    "tree_token_walk",
+    "tree_select_subtree",
     "ta_status_string",
     "ta_version",
     "ta_last_error",
@@ -103,6 +105,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.tree_expand_top_w.restype = c_int
         lib.tree_expand_top_w_workspace_bytes.argtypes = [c_int, c_int, c_int]
         lib.tree_expand_top_w_workspace_bytes.restype = c_size
+        lib.tree_token_walk.argtypes = [vp] * 5 + [c_int] * 3 + [vp] * 4
+        lib.tree_token_walk.restype = c_int
+        lib.tree_select_subtree.argtypes = [vp] * 4 + [c_int] * 3 + [vp] * 5
+        lib.tree_select_subtree.restype = c_int
         lib.ta_status_string.argtypes = [c_int]
         lib.ta_status_string.restype = ctypes.c_char_p
         lib.ta_version.argtypes = []
@@ -445,3 +451,71 @@ def tree_expand_top_w(logits, parent, tok, cum, n_nodes, w: int, workspace=None,
                                int(w), _ptr(ws), ws_bytes, _stream(stream))
     _check(st)
     return n_nodes
+
+
+def tree_token_walk(parent, tok, n_nodes, verified, verified_len, path=None, path_len=None,
+                    keep=None, stream=None):
+    """Walk the draft tree along the verified tokens; returns ``(path,
+    path_len, keep)``, the re-root arguments of ``tree_cache_reroot``."""
+    torch = _torch()
+    lib = load_library()
+    _need(parent, "parent", dtype=torch.int32, ndim=2)
+    dev = parent.device
+    _need(tok, "tok", dtype=torch.int32, ndim=2, device=dev)
+    _need(n_nodes, "n_nodes", dtype=torch.int32, ndim=1, device=dev)
+    _need(verified, "verified", dtype=torch.int32, ndim=2, device=dev)
+    _need(verified_len, "verified_len", dtype=torch.int32, ndim=1, device=dev)
+    B, n_max = (int(x) for x in parent.shape)
+    m_max = int(verified.shape[1])
+    if tuple(tok.shape) != (B, n_max) or n_nodes.shape[0] != B:
+        raise ValueError("tok must be [B][n_max] and n_nodes [B]")
+    if verified.shape[0] != B or verified_len.shape[0] != B:
+        raise ValueError("verified must be [B][m_max] and verified_len [B]")
+    if path is None:
+        path = torch.empty((B, n_max), dtype=torch.int32, device=dev)
+    if path_len is None:
+        path_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    if keep is None:
+        keep = torch.empty((B,), dtype=torch.uint8, device=dev)
+    _need(path, "path", dtype=torch.int32, ndim=2, device=dev)
+    _need(path_len, "path_len", dtype=torch.int32, ndim=1, device=dev)
+    _need(keep, "keep", dtype=torch.uint8, ndim=1, device=dev)
+    if tuple(path.shape) != (B, n_max) or path_len.shape[0] != B or keep.shape[0] != B:
+        raise ValueError("path must be [B][n_max], path_len and keep [B]")
+    st = lib.tree_token_walk(parent.data_ptr(), tok.data_ptr(), n_nodes.data_ptr(),
+                             verified.data_ptr(), verified_len.data_ptr(), B, n_max, m_max,
+                             path.data_ptr(), path_len.data_ptr(), keep.data_ptr(), _stream(stream))
+    _check(st)
+    return path, path_len, keep
+
+
+def tree_select_subtree(cum, parent, tok, n_nodes, bs: int, sel_node=None, sel_parent=None,
+                        sel_tok=None, sel_n=None, stream=None):
+    """The subtree of ``bs`` nodes to send; returns ``(sel_node, sel_parent,
+    sel_tok, sel_n)`` ([B][bs], [B][bs], [B][bs], [B])."""
+    torch = _torch()
+    lib = load_library()
+    _need(cum, "cum", dtype=torch.float32, ndim=2)
+    dev = cum.device
+    _need(parent, "parent", dtype=torch.int32, ndim=2, device=dev)
+    _need(tok, "tok", dtype=torch.int32, ndim=2, device=dev)
+    _need(n_nodes, "n_nodes", dtype=torch.int32, ndim=1, device=dev)
+    B, n_max = (int(x) for x in cum.shape)
+    bs = int(bs)
+    if tuple(parent.shape) != (B, n_max) or tuple(tok.shape) != (B, n_max) or n_nodes.shape[0] != B:
+        raise ValueError("parent/tok must be [B][n_max] like cum, n_nodes [B]")
+    outs = []
+    for t, name, shape in ((sel_node, "sel_node", (B, bs)), (sel_parent, "sel_parent", (B, bs)),
+                           (sel_tok, "sel_tok", (B, bs)), (sel_n, "sel_n", (B,))):
+        if t is None:
+            t = torch.empty(shape, dtype=torch.int32, device=dev)
+        _need(t, name, dtype=torch.int32, ndim=len(shape), device=dev)
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} must have shape {shape}")
+        outs.append(t)
+    st = lib.tree_select_subtree(cum.data_ptr(), parent.data_ptr(), tok.data_ptr(),
+                                 n_nodes.data_ptr(), B, n_max, bs, outs[0].data_ptr(),
+                                 outs[1].data_ptr(), outs[2].data_ptr(), outs[3].data_ptr(),
+                                 _stream(stream))
+    _check(st)
+    return tuple(outs)

@@ -296,6 +296,37 @@ int accept_greedy_path(const void* logits, int logit_dtype, const int32_t* paren
   return hip_status(e, "accept_greedy_path launch");
 }
 
+int tree_token_walk(const int32_t* parent, const int32_t* tok, const int32_t* n_nodes,
+                    const int32_t* verified, const int32_t* verified_len, int B, int n_max,
+                    int m_max, int32_t* path, int32_t* path_len, uint8_t* keep, void* stream) {
+  if (B < 0 || n_max < 1 || m_max < 1) return TA_ERR_INVALID_ARG;
+  if (n_max > TA_MAX_NODES) return TA_ERR_TREE_TOO_LARGE;
+  if (m_max > ta::kWalkMaxTokens) return TA_ERR_UNSUPPORTED;
+  if (parent == nullptr || tok == nullptr || n_nodes == nullptr || verified == nullptr ||
+      verified_len == nullptr || path == nullptr || path_len == nullptr || keep == nullptr)
+    return TA_ERR_INVALID_ARG;
+  if (B == 0) return TA_OK;
+  hipError_t e = ta::launch_token_walk(parent, tok, n_nodes, verified, verified_len, B, n_max,
+                                       m_max, path, path_len, keep,
+                                       static_cast<hipStream_t>(stream));
+  return hip_status(e, "tree_token_walk launch");
+}
+
+int tree_select_subtree(const float* cum, const int32_t* parent, const int32_t* tok,
+                        const int32_t* n_nodes, int B, int n_max, int bs, int32_t* sel_node,
+                        int32_t* sel_parent, int32_t* sel_tok, int32_t* sel_n, void* stream) {
+  if (B < 0 || n_max < 1 || bs < 1 || bs > n_max) return TA_ERR_INVALID_ARG;
+  if (n_max > TA_MAX_NODES) return TA_ERR_TREE_TOO_LARGE;
+  if (cum == nullptr || parent == nullptr || tok == nullptr || n_nodes == nullptr ||
+      sel_node == nullptr || sel_parent == nullptr || sel_tok == nullptr || sel_n == nullptr)
+    return TA_ERR_INVALID_ARG;
+  if (B == 0) return TA_OK;
+  hipError_t e = ta::launch_select_subtree(cum, parent, tok, n_nodes, B, n_max, bs, sel_node,
+                                           sel_parent, sel_tok, sel_n,
+                                           static_cast<hipStream_t>(stream));
+  return hip_status(e, "tree_select_subtree launch");
+}
+
 int tree_cache_reroot(const ta_kv* kv_layers, int n_layers, int32_t* prefix_len, int32_t* parent,
                       int32_t* n_nodes, const int32_t* path, const int32_t* path_len,
                       const uint8_t* keep_subtree, int B, int n_max, int Hkv, int d, int dtype,

@@ -99,6 +99,18 @@ hipError_t launch_topw(const void* logits, int logit_dtype, int32_t* parent, int
                        float* cum, int32_t* n_nodes, int B, int n_max, int V, int w, void* ws,
                        hipStream_t s);
 
+// Draft side of an iteration: the walk along the verified tokens (re-root
+// path and keep flag) and the choice of the size-bs subtree to send.
+constexpr int kWalkMaxTokens = 1024;
+hipError_t launch_token_walk(const int32_t* parent, const int32_t* tok, const int32_t* n_nodes,
+                             const int32_t* verified, const int32_t* verified_len, int B,
+                             int n_max, int m_max, int32_t* path, int32_t* path_len,
+                             uint8_t* keep, hipStream_t s);
+hipError_t launch_select_subtree(const float* cum, const int32_t* parent, const int32_t* tok,
+                                 const int32_t* n_nodes, int B, int n_max, int bs,
+                                 int32_t* sel_node, int32_t* sel_parent, int32_t* sel_tok,
+                                 int32_t* sel_n, hipStream_t s);
+
 // Re-root: one launch per group of layers moves rows, then one updates metadata.
 constexpr int kRerootMaxLayersPerLaunch = 32;
 struct RerootLayer {
