@@ -30,7 +30,10 @@ Other workloads (``--workload``), each printing the same kind of line:
                      grown by 4 rounds of 8 new leaves; each round selects the
                      leaves on the device (tree_expand_top_w over the root's
                      and every node's 32000-way distribution) and attends them
-                     (tree_attn_expand), on KV copy s mod 64 (563 MB in all).
+                     (tree_attn_expand), on KV copy s mod 64 (563 MB in all);
+                     then the walk along the verified tokens and the choice of
+                     the bs = 8 nodes to send (tree_token_walk,
+                     tree_select_subtree).
 
 Prints one JSON line (metric, value = microseconds per step, roofline of the
 attention call, CPU-oracle baseline on a bounded sample).
@@ -335,13 +338,19 @@ class DraftExpand(_Workload):
     """Four expansion rounds over a 64-node draft tree, all on the device: each
     round tree_expand_top_w appends the w = 8 best leaves (maximum-likelihood
     expansion over the 32000-way rows of the root and every node), then
-    tree_attn_expand attends the new leaves over prefix + tree.  The tree is
-    restored after the step (one elementwise kernel), so every step grows the
-    same tree.  Phases (HIP-graph mode): "expand" = the 4 attention calls, on
-    the trees the rounds produce; "topw" = one restore + the 4 selections.
-    With --eager the phases are not separated (the whole step is "expand")."""
-    phases = ("expand", "topw")
+    tree_attn_expand attends the new leaves over prefix + tree.  Then the
+    draft side of the iteration: tree_token_walk along the target's verified
+    tokens (a root path of the grown tree, fixed once the first step has run)
+    and tree_select_subtree of the bs = 8 nodes to send.  The tree is restored
+    after the step (one elementwise kernel), so every step grows the same
+    tree.  Phases (HIP-graph mode): "expand" = the 4 attention calls, on the
+    trees the rounds produce; "topw" = one restore + the 4 selections;
+    "walk_select" = the walk and the selection on the grown tree.  With
+    --eager the phases are not separated (the whole step is "expand")."""
+    phases = ("expand", "topw", "walk_select")
     COPIES = 64
+    BS = 8       # nodes sent to the target per iteration
+    M_VER = 8    # room for the verified tokens
 
     def __init__(self, ta, up):
         import numpy as np
@@ -381,6 +390,14 @@ class DraftExpand(_Workload):
         self.lses = [torch.empty((1, e.Hq, e.w), dtype=torch.float32, device=up.dev)
                      for _ in self.qs]
         self.snaps = None   # per-round (parent, n) after its selection, for the expand phase
+        self.final = None   # (parent, tok, cum, n) of the grown tree
+        i32 = dict(dtype=torch.int32, device=up.dev)
+        self.verified = torch.zeros((1, self.M_VER), **i32)
+        self.vlen = torch.zeros((1,), **i32)
+        self.walk_out = (torch.empty((1, nm), **i32), torch.empty((1,), **i32),
+                         torch.empty((1,), dtype=torch.uint8, device=up.dev))
+        self.sel_out = (torch.empty((1, self.BS), **i32), torch.empty((1, self.BS), **i32),
+                        torch.empty((1, self.BS), **i32), torch.empty((1,), **i32))
         self.topw_ws = ta.Workspace(up.dev)
         b = [attn_bytes([e.P], [e.n0 + e.w * (r + 1)], [e.w], e.Hq, e.Hkv, e.d)
              for r in range(e.rounds)]
@@ -388,7 +405,10 @@ class DraftExpand(_Workload):
         self.config = {"workload": "draft_expand", "batch": 1, "Hq": e.Hq, "Hkv": e.Hkv,
                        "head_dim": e.d, "prefix": e.P, "tree_nodes": f"{e.n0}->{e.n_max}",
                        "w": e.w, "rounds": e.rounds, "vocab": e.vocab, "kv_copies": self.COPIES,
-                       "step": "4 rounds of top-w selection + expansion attention (+ tree restore)"}
+                       "bs": self.BS,
+                       "step": "4 rounds of top-w selection + expansion attention, then the walk "
+                               "along the verified tokens and the size-bs subtree selection "
+                               "(+ tree restore)"}
 
     @staticmethod
     def _cum0(e):
@@ -417,12 +437,17 @@ class DraftExpand(_Workload):
     def _restore(self):
         self.torch.add(self.meta0, 0, out=self.meta)
 
+    def _draft_side(self, par, tok, cum, n):
+        self.ta.tree_token_walk(par, tok, n, self.verified, self.vlen, *self.walk_out)
+        self.ta.tree_select_subtree(cum, par, tok, n, self.BS, *self.sel_out)
+
     def step(self, i, ws, marks, opts):
         kv = self.kvs[i % self.COPIES]
         if marks is not None:
             marks[0].record()
         for r in range(self.e.rounds):
             self._round(r, kv, ws, opts)
+        self._draft_side(self.par, self.tok, self.cum, self.n)
         self._restore()
         if marks is not None:
             marks[1].record()
@@ -437,6 +462,7 @@ class DraftExpand(_Workload):
             self.ta.tree_expand_top_w(self.logits, self.par, self.tok, self.cum, self.n,
                                       self.e.w, workspace=self.topw_ws)
             snaps.append((self.par.clone(), self.n.clone()))
+        self.final = (self.par.clone(), self.tok.clone(), self.cum.clone(), self.n.clone())
         self._restore()
         torch.cuda.synchronize()
         return snaps
@@ -449,11 +475,13 @@ class DraftExpand(_Workload):
             for r, (par, n) in enumerate(self.snaps):
                 self.ta.tree_attn_expand(self.qs[r], kv, self.P, par, n, self.e.scale,
                                          out=self.outs[r], lse=self.lses[r], workspace=ws, **opts)
-        else:
+        elif j == 1:
             self._restore()
             for r in range(self.e.rounds):
                 self.ta.tree_expand_top_w(self.logits, self.par, self.tok, self.cum, self.n,
                                           self.e.w, workspace=self.topw_ws)
+        else:
+            self._draft_side(*self.final)
 
     def attn_bytes(self, i):
         return self.bytes
@@ -465,9 +493,27 @@ class DraftExpand(_Workload):
                 raise RuntimeError("non-finite expansion output")
         if self.snaps is None:
             self.snaps = self._snapshots(None, None)
+            self._set_verified()
         e = self.e
         if int(self.snaps[-1][1].item()) != e.n0 + e.w * e.rounds:
             raise RuntimeError("the expansion rounds did not grow the tree to its full size")
+
+    def _set_verified(self):
+        """The target's verified tokens: the root path of the grown tree's
+        best node (largest cumulative score) at depth 4 or less."""
+        import numpy as np
+
+        import oracle
+        par, tok, cum, n = (t.cpu().numpy() for t in self.final)
+        n = int(n[0])
+        par, tok, cum = par[0], tok[0], cum[0]
+        cand = [i for i in range(n) if oracle.depth(par, i) <= min(4, self.M_VER)]
+        best = max(cand, key=lambda i: (float(cum[i]), -i))
+        ver = [int(tok[v]) for v in oracle.root_path(par, best)]
+        self.verified.zero_()
+        self.verified[0, :len(ver)] = self.torch.tensor(ver, dtype=self.torch.int32)
+        self.vlen.fill_(len(ver))
+        self.torch.cuda.synchronize()
 
     def cpu_baseline(self, budget):
         """The oracle for one step: per round, top-w selection (fp64) and the
@@ -491,9 +537,14 @@ class DraftExpand(_Workload):
             oc.parent, oc.n_nodes = par[None].copy(), np.array([n])
             oracle.expand(oc, e.q_new[r], e.w)
             rows = np.concatenate([rows, e.logits_new[r]])
+        ver = self.verified[0, :int(self.vlen.item())].cpu().numpy()
+        oracle.token_walk(par, tok, n, ver)
+        oracle.select_subtree(par, tok, oracle.cumulative_scores(par, tok, e.logits_root, rows[:n], n),
+                              n, self.BS)
         dt = time.perf_counter() - t0
         return {"value": dt * 1e6, "unit": "us/step", "cores": _blas_threads(), "kind": "oracle",
-                "sample": "all 4 rounds of one step (top-w selection + expansion attention)",
+                "sample": "all 4 rounds of one step (top-w selection + expansion attention) "
+                          "and the walk + subtree selection",
                 "host_cpus": len(os.sched_getaffinity(0))}
 
     def c_like(self):
