@@ -26,6 +26,8 @@ Modules:
   expansion rounds).
 * ``draft``     -- the draft side's walk along the verified tokens and the
   choice of the subtree to send (Algorithm 1, Re-root and Select).
+* ``rope``      -- rotary position embedding at tree positions and the KV
+  append of the new nodes.
 * ``bf16``      -- exact bfloat16 -> float64 decoding.
 
 Pins: every function here is checked in ``tests/test_oracle_*.py`` against
@@ -41,3 +43,4 @@ from .accept import accept_greedy_path, argmax_first  # noqa: F401
 from .reroot import tree_cache_reroot  # noqa: F401
 from .topw import cumulative_scores, select_top_w  # noqa: F401
 from .draft import token_walk, select_subtree  # noqa: F401
+from .rope import rope, tree_positions, rope_append  # noqa: F401
