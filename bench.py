@@ -225,6 +225,10 @@ class _VerifyBatch:
 
 
 class _Workload:
+    def extras(self):
+        """Calls timed beside the step (name -> fn(i, ws, opts)); none by default."""
+        return {}
+
     def step(self, i, ws, marks, opts):
         for j in range(len(self.phases)):
             if marks is not None:
@@ -242,6 +246,7 @@ class ChainVerify(_Workload):
         c = self.c = config2_chain()
         self.batch = _VerifyBatch(ta, up, c, ta.KVCache(up(c.k, True), up(c.v, True)),
                                   up(c.q, True))
+        self._rope = None
         self.config = {"workload": "chain_verify", "batch": c.B, "Hq": c.Hq, "Hkv": c.Hkv,
                        "head_dim": c.d, "prefix": int(c.prefix_len[0]), "D": c.n_max - 1,
                        "rows_per_kv_head": c.G * c.n_max, "vocab": c.vocab,
@@ -249,6 +254,25 @@ class ChainVerify(_Workload):
 
     def phase(self, i, j, ws, opts):
         self.batch.phase(j, ws, opts)
+
+    def extras(self):
+        """RoPE at the tree positions and the KV append of the 16 nodes per
+        sequence (tree_rope_append), timed beside the step: the workload's
+        queries and tree keys stand in for un-rotated ones, and the rotated
+        keys overwrite the tree rows (so this runs after everything else)."""
+        import torch
+        bt, c = self.batch, self.c
+        if self._rope is None:
+            k_new = torch.stack([bt.kv.k[b, int(c.prefix_len[b]):int(c.prefix_len[b]) + c.n_max]
+                                 for b in range(c.B)]).contiguous()
+            v_new = torch.stack([bt.kv.v[b, int(c.prefix_len[b]):int(c.prefix_len[b]) + c.n_max]
+                                 for b in range(c.B)]).contiguous()
+            self._rope = (k_new, v_new, torch.empty_like(bt.q))
+        k_new, v_new, q_out = self._rope
+
+        def rope(i, ws, opts):
+            bt.ta.tree_rope_append(bt.q, k_new, v_new, bt.kv, bt.P, bt.par, bt.n, q_out=q_out)
+        return {"rope_append": rope}
 
     def attn_bytes(self, i):
         return self.batch.bytes
@@ -675,6 +699,7 @@ def main(argv=None):
         ms_per_step = start.elapsed_time(stop) / a.steps
         w.check()
         phase_ms = []
+        extra_ms = {}
         for j in range(nph):
             g = capture(lambda: [w.phase(i, j, ws, opts) for i in steps])
             g.replay()
@@ -688,6 +713,22 @@ def main(argv=None):
                 torch.cuda.synchronize()
                 per_call.append(e0.elapsed_time(e1) / a.steps)
             phase_ms.append(per_call)
+            del g
+        # Calls timed beside the step (not part of it), the same way, last:
+        # they may rewrite the inputs.
+        for name, fn in w.extras().items():
+            g = capture(lambda: [fn(i, ws, opts) for i in steps])
+            g.replay()
+            per_call = []
+            for _ in range(PHASE_REPS):
+                e0, e1 = ev(), ev()
+                torch.cuda.synchronize()
+                e0.record()
+                g.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                per_call.append(e0.elapsed_time(e1) / a.steps)
+            extra_ms[name] = per_call
             del g
         del g_steps
     attn_ms = phase_ms[0]
@@ -731,6 +772,10 @@ def main(argv=None):
     }
     for j in range(1, nph):
         res[f"{w.phases[j]}_us"] = round(med(phase_ms[j]) * 1e3, 2)
+    for name, ms in extra_ms.items():
+        res[f"{name}_us"] = round(med(ms) * 1e3, 2)
+    if extra_ms:
+        res["beside_step"] = sorted(f"{name}_us" for name in extra_ms)
     res["device_copy_GBps"] = round(2 * (1 << 30) / copy_s / 1e9, 1)
     res["roofline"] = roofline
     if not a.no_cpu_baseline:

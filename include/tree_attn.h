@@ -220,6 +220,32 @@ int tree_expand_top_w(const void* logits, int logit_dtype, int32_t* parent, int3
 size_t tree_expand_top_w_workspace_bytes(int B, int n_max, int w);
 
 /*
+ * Rotary position embedding at tree positions and the KV append of the new
+ * nodes ([SS] Section 3.3: the masked attention takes the position
+ * embedding, RoPE; Section 3.2: a node's KV stays where it was computed).
+ * Run before tree_attn_verify / tree_attn_expand, which take rotated Q and K.
+ *
+ *   q, q_out     [B][n_q][Hq][d]  query rows, un-rotated in, rotated out (may
+ *                alias); slot s holds node s (expand = 0) or node
+ *                n_nodes[b] - n_q + s (expand = 1)
+ *   k_new, v_new [B][n_q][Hkv][d] the same slots' keys (un-rotated) and values
+ *   kv           the cache: the rotated key and the value of the node in slot
+ *                s go to row prefix_len[b] + node (layouts as for
+ *                tree_attn_verify)
+ *   prefix_len, parent, n_nodes: as for tree_attn_verify (device)
+ *
+ * Node i sits at position P - 1 + depth(i) (a child of the root at P, where P
+ * = prefix_len[b]); channel pair (j, j + d/2), j < d/2, turns by position *
+ * base^(-2j/d) ("rotate half").  Angles are reduced in double precision, the
+ * rotation is done in fp32 and stored in dtype.  Slots without a node are not
+ * written.  1 <= n_q <= n_max; base > 0.
+ */
+int tree_rope_append(const void* q, void* q_out, const void* k_new, const void* v_new, ta_kv kv,
+                     const int32_t* prefix_len, const int32_t* parent, const int32_t* n_nodes,
+                     int B, int n_q, int n_max, int expand, int Hq, int Hkv, int d, int dtype,
+                     float base, void* stream);
+
+/*
  * Draft-side walk along the target's verified tokens ([SS] Section 3.1.1
  * Algorithm 1, Synchronize and Re-root; Section 3.2 update procedure;
  * Section 3.1.2 Figure 2).

@@ -185,3 +185,30 @@ def test_draft_side_host_side_validation():
         ptrs = [P] * 8
         ptrs[i] = None
         assert select(ptrs=tuple(ptrs)) == _lib.TA_ERR_INVALID_ARG, i
+
+
+def test_rope_append_host_side_validation():
+    lib = ensure_built()
+    P = 0x4000
+
+    def call(B=2, n_q=16, n_max=16, expand=0, Hq=8, Hkv=2, d=128, dt=ta.TA_BF16, base=1e4,
+             ptrs=(P,) * 7, kv=None):
+        kv = kv if kv is not None else _kv()
+        return lib.tree_rope_append(ptrs[0], ptrs[1], ptrs[2], ptrs[3], kv, ptrs[4], ptrs[5],
+                                    ptrs[6], B, n_q, n_max, expand, Hq, Hkv, d, dt,
+                                    ctypes.c_float(base), None)
+
+    assert call(B=0) == _lib.TA_OK
+    assert call(Hq=7) == _lib.TA_ERR_INVALID_ARG
+    assert call(d=96) == _lib.TA_ERR_UNSUPPORTED
+    assert call(dt=7) == _lib.TA_ERR_UNSUPPORTED
+    assert call(n_max=257, n_q=16) == _lib.TA_ERR_TREE_TOO_LARGE
+    assert call(n_q=17) == _lib.TA_ERR_INVALID_ARG
+    assert call(expand=2) == _lib.TA_ERR_INVALID_ARG
+    for bad in (0.0, -1.0, float("nan"), float("inf")):
+        assert call(base=bad) == _lib.TA_ERR_INVALID_ARG, bad
+    assert call(kv=_lib.ta_kv(0x1000, None, None, 0, 0, 0, 64)) == _lib.TA_ERR_INVALID_ARG
+    for i in range(7):
+        ptrs = [P] * 7
+        ptrs[i] = None
+        assert call(ptrs=tuple(ptrs)) == _lib.TA_ERR_INVALID_ARG, i

@@ -9,6 +9,7 @@ entry points keep the C names:
 * ``accept_greedy_path`` -- greedy longest accepted path, AL and bonus token
 * ``tree_cache_reroot``  -- evolving-tree-cache re-root with in-place KV moves
 * ``tree_expand_top_w``  -- maximum-likelihood expansion: append the w best leaves
+* ``tree_rope_append``   -- RoPE at tree positions + KV append of the new nodes
 * ``tree_token_walk``    -- draft side: walk along the verified tokens (re-root path)
 * ``tree_select_subtree``-- draft side: the size-bs subtree to send
 """
@@ -31,6 +32,7 @@ from ._lib import (  # noqa: F401
     tree_cache_reroot,
     tree_expand_top_w,
     tree_expand_top_w_workspace_bytes,
+    tree_rope_append,
     tree_select_subtree,
     tree_token_walk,
 )

@@ -34,6 +34,7 @@ EXPORTED_SYMBOLS = (
     "tree_cache_reroot",
     "tree_expand_top_w",
     "tree_expand_top_w_workspace_bytes",
+    "tree_rope_append",
     "tree_token_walk",
     "tree_select_subtree",
     "ta_status_string",
@@ -105,6 +106,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.tree_expand_top_w.restype = c_int
         lib.tree_expand_top_w_workspace_bytes.argtypes = [c_int, c_int, c_int]
         lib.tree_expand_top_w_workspace_bytes.restype = c_size
+        lib.tree_rope_append.argtypes = [vp] * 4 + [ta_kv] + [vp] * 3 + [c_int] * 8 + [f32, vp]
+        lib.tree_rope_append.restype = c_int
         lib.tree_token_walk.argtypes = [vp] * 5 + [c_int] * 3 + [vp] * 4
         lib.tree_token_walk.restype = c_int
         lib.tree_select_subtree.argtypes = [vp] * 4 + [c_int] * 3 + [vp] * 5
@@ -519,3 +522,38 @@ def tree_select_subtree(cum, parent, tok, n_nodes, bs: int, sel_node=None, sel_p
                                  _stream(stream))
     _check(st)
     return tuple(outs)
+
+
+def tree_rope_append(q, k_new, v_new, kv: "KVCache", prefix_len, parent, n_nodes,
+                     base: float = 10000.0, expand: bool = False, q_out=None, stream=None):
+    """RoPE of the query rows and the new nodes' keys at their tree positions,
+    and the append of those keys and values to the cache; returns the rotated
+    queries (``q_out``, which may be ``q`` itself)."""
+    torch = _torch()
+    lib = load_library()
+    _need(q, "q", ndim=4)
+    dev = q.device
+    B, n_q, Hq, d = (int(x) for x in q.shape)
+    _need(k_new, "k_new", dtype=q.dtype, ndim=4, device=dev)
+    _need(v_new, "v_new", dtype=q.dtype, ndim=4, device=dev)
+    if tuple(k_new.shape) != (B, n_q, kv.Hkv, d) or tuple(v_new.shape) != tuple(k_new.shape):
+        raise ValueError("k_new and v_new must be [B][n_q][Hkv][d]")
+    if kv.dtype != q.dtype or kv.d != d:
+        raise ValueError("the cache must match q in dtype and head size")
+    _need(prefix_len, "prefix_len", dtype=torch.int32, ndim=1, device=dev)
+    _need(parent, "parent", dtype=torch.int32, ndim=2, device=dev)
+    _need(n_nodes, "n_nodes", dtype=torch.int32, ndim=1, device=dev)
+    n_max = int(parent.shape[1])
+    if parent.shape[0] != B or prefix_len.shape[0] != B or n_nodes.shape[0] != B:
+        raise ValueError("prefix_len, parent and n_nodes must have B rows")
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    _need(q_out, "q_out", dtype=q.dtype, ndim=4, device=dev)
+    if tuple(q_out.shape) != tuple(q.shape):
+        raise ValueError("q_out must have the shape of q")
+    st = lib.tree_rope_append(q.data_ptr(), q_out.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+                              kv.struct(), prefix_len.data_ptr(), parent.data_ptr(),
+                              n_nodes.data_ptr(), B, n_q, n_max, int(bool(expand)), Hq, kv.Hkv,
+                              d, _dtype_code(q), ctypes.c_float(base), _stream(stream))
+    _check(st)
+    return q_out

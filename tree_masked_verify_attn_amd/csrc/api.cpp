@@ -296,6 +296,47 @@ int accept_greedy_path(const void* logits, int logit_dtype, const int32_t* paren
   return hip_status(e, "accept_greedy_path launch");
 }
 
+int tree_rope_append(const void* q, void* q_out, const void* k_new, const void* v_new, ta_kv kv,
+                     const int32_t* prefix_len, const int32_t* parent, const int32_t* n_nodes,
+                     int B, int n_q, int n_max, int expand, int Hq, int Hkv, int d, int dtype,
+                     float base, void* stream) {
+  int st = check_common(B, n_q, n_max, Hq, Hkv, d, dtype, kv.T_cap);
+  if (st != TA_OK) return st;
+  st = check_kv(kv);
+  if (st != TA_OK) return st;
+  if (n_q > n_max || (expand != 0 && expand != 1)) return TA_ERR_INVALID_ARG;
+  if (!(base > 0.f) || base != base || base == INFINITY) return TA_ERR_INVALID_ARG;
+  if (q == nullptr || q_out == nullptr || k_new == nullptr || v_new == nullptr ||
+      prefix_len == nullptr || parent == nullptr || n_nodes == nullptr)
+    return TA_ERR_INVALID_ARG;
+  if (B == 0) return TA_OK;
+  ta::RopeParams p{};
+  p.q_in = q;
+  p.q_out = q_out;
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.k = kv.k;
+  p.v = kv.v;
+  p.block_table = kv.block_table;
+  p.block_size = kv.block_size;
+  p.max_blocks = kv.max_blocks;
+  p.num_blocks = kv.num_blocks;
+  p.T_cap = kv.T_cap;
+  p.prefix_len = prefix_len;
+  p.parent = parent;
+  p.n_nodes = n_nodes;
+  p.B = B;
+  p.n_q = n_q;
+  p.n_max = n_max;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.d = d;
+  p.expand = expand;
+  p.base = base;
+  hipError_t e = ta::launch_rope_append(p, dtype, static_cast<hipStream_t>(stream));
+  return hip_status(e, "tree_rope_append launch");
+}
+
 int tree_token_walk(const int32_t* parent, const int32_t* tok, const int32_t* n_nodes,
                     const int32_t* verified, const int32_t* verified_len, int B, int n_max,
                     int m_max, int32_t* path, int32_t* path_len, uint8_t* keep, void* stream) {

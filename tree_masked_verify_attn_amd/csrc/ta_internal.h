@@ -99,6 +99,25 @@ hipError_t launch_topw(const void* logits, int logit_dtype, int32_t* parent, int
                        float* cum, int32_t* n_nodes, int B, int n_max, int V, int w, void* ws,
                        hipStream_t s);
 
+// RoPE at tree positions (P - 1 + depth) of the query rows and the new nodes'
+// keys, and the append of those keys and values to cache rows P + node.
+struct RopeParams {
+  const void* q_in;
+  void* q_out;
+  const void* k_new;
+  const void* v_new;
+  void* k;
+  void* v;
+  const int32_t* block_table;
+  int32_t block_size, max_blocks, num_blocks, T_cap;
+  const int32_t* prefix_len;
+  const int32_t* parent;
+  const int32_t* n_nodes;
+  int32_t B, n_q, n_max, Hq, Hkv, d, expand;
+  float base;
+};
+hipError_t launch_rope_append(const RopeParams& p, int dtype, hipStream_t s);
+
 // Draft side of an iteration: the walk along the verified tokens (re-root
 // path and keep flag) and the choice of the size-bs subtree to send.
 constexpr int kWalkMaxTokens = 1024;
