@@ -12,6 +12,8 @@ Sources (the pages are cited by title and section/figure):
   maximum-likelihood expansion (Section 3.1.3), evolving tree cache invariant
   and re-root (Section 3.2, Figure 4), iteration example (Section 3.1.2,
   Figure 2).
+* "MineDraft notes": the residual distribution a rejected draft token is
+  resampled from (the PEARL walkthrough), sampling at temperature 1.0.
 * "Draft-length co-design" article: acceptance up to the first mismatch plus
   the target's own token, AL in [1, 1+D], G x (1+D) query rows per KV head
   (its "key mechanism" and "how speculative decoding works" parts).
@@ -28,6 +30,8 @@ Modules:
   choice of the subtree to send (Algorithm 1, Re-root and Select).
 * ``rope``      -- rotary position embedding at tree positions and the KV
   append of the new nodes.
+* ``sampling``  -- tree verification by speculative sampling (temperature
+  > 0, residual resampling on rejection).
 * ``bf16``      -- exact bfloat16 -> float64 decoding.
 
 Pins: every function here is checked in ``tests/test_oracle_*.py`` against
@@ -44,3 +48,4 @@ from .reroot import tree_cache_reroot  # noqa: F401
 from .topw import cumulative_scores, select_top_w  # noqa: F401
 from .draft import token_walk, select_subtree  # noqa: F401
 from .rope import rope, tree_positions, rope_append  # noqa: F401
+from .sampling import accept_sampling_path, residual, sample_inverse_cdf, softmax_t  # noqa: F401
