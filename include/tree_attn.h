@@ -188,6 +188,45 @@ int tree_cache_reroot(const ta_kv* kv_layers, int n_layers, int32_t* prefix_len,
                       void* stream);
 
 /*
+ * Tree verification by speculative sampling, temperature > 0 ([MD] the
+ * PEARL walkthrough: a rejected draft token is replaced by a draw from
+ * norm(max(0, p - q)); [MD] experimental setup: sampling at temperature
+ * 1.0; [SS] Section 3.1: the draft tree).
+ *
+ *   target_logits, draft_logits [B][n_max][V] fp32 or bf16 (logit_dtype):
+ *            row i is the target's / the draft's distribution after node i
+ *   parent, tok, n_nodes, root_tok: as for accept_greedy_path (device)
+ *   u_accept [B][n_max] fp32: a uniform number in [0, 1) per node, used
+ *            when that node is tested; u_bonus [B] fp32: one per sequence
+ *            for the bonus draw (the caller draws them)
+ *   path, path_len, bonus: outputs as for accept_greedy_path
+ *
+ * With p = softmax(target row / T) and q = softmax(draft row / T) at an
+ * accepted node: the walk starts at the lowest-index node with parent -1
+ * whose token is root_tok (none: path_len 0, bonus = root_tok); the node's
+ * children are tried in index order against r (first p): child c with token
+ * x is accepted when u_accept[c] * q(x) < r(x) and the walk moves to it; a
+ * rejection sets r = norm(max(0, r - q)) (unchanged if that sums to 0).
+ * When no child is accepted the bonus is the smallest token t whose running
+ * sum of r exceeds u_bonus * sum(r).  Drawn this way, with the tree's
+ * siblings independent draws from q, every emitted token follows the
+ * target's distribution.  Arithmetic is fp32; logits must be finite;
+ * 0 < temperature < inf.  ws holds accept_sampling_workspace_bytes bytes
+ * (16-byte aligned; calls that overlap in time must not share it).  A node
+ * with k rejected children costs k passes over its two rows (k steps per
+ * element each).
+ */
+int accept_sampling_path(const void* target_logits, const void* draft_logits, int logit_dtype,
+                         const int32_t* parent, const int32_t* tok, const int32_t* n_nodes,
+                         const int32_t* root_tok, const float* u_accept, const float* u_bonus,
+                         float temperature, int B, int n_max, int V, int32_t* path,
+                         int32_t* path_len, int32_t* bonus, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/* Workspace (bytes) for accept_sampling_path, or (size_t)-1 for invalid sizes. */
+size_t accept_sampling_workspace_bytes(int B, int n_max);
+
+/*
  * Maximum-likelihood draft-tree expansion step ([SS] Section 3.1.3: a node's
  * value is the log-softmax probability of its token under its parent's
  * distribution, its weight the sum of the values from the root down to it;

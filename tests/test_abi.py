@@ -212,3 +212,32 @@ def test_rope_append_host_side_validation():
         ptrs = [P] * 7
         ptrs[i] = None
         assert call(ptrs=tuple(ptrs)) == _lib.TA_ERR_INVALID_ARG, i
+
+
+def test_accept_sampling_host_side_validation():
+    lib = ensure_built()
+    P = 0x4000
+    ws_need = lib.accept_sampling_workspace_bytes(4, 16)
+    assert ws_need == 4 * 16 * 16
+    assert lib.accept_sampling_workspace_bytes(4, 257) == ctypes.c_size_t(-1).value
+    assert lib.accept_sampling_workspace_bytes(-1, 16) == ctypes.c_size_t(-1).value
+
+    def call(B=4, n_max=16, V=1000, dt=ta.TA_BF16, T=1.0, ptrs=(P,) * 13, ws=P, ws_bytes=ws_need):
+        return lib.accept_sampling_path(ptrs[0], ptrs[1], dt, ptrs[2], ptrs[3], ptrs[4], ptrs[5],
+                                        ptrs[6], ptrs[7], ctypes.c_float(T), B, n_max, V, ptrs[8],
+                                        ptrs[9], ptrs[10], ws, ws_bytes, None)
+
+    assert call(B=0) == _lib.TA_OK
+    assert call(B=-1) == _lib.TA_ERR_INVALID_ARG
+    assert call(V=0) == _lib.TA_ERR_INVALID_ARG
+    assert call(n_max=257) == _lib.TA_ERR_TREE_TOO_LARGE
+    assert call(dt=5) == _lib.TA_ERR_UNSUPPORTED
+    for bad in (0.0, -1.0, float("nan"), float("inf"), 1e-45):
+        assert call(T=bad) == _lib.TA_ERR_INVALID_ARG, bad
+    for i in range(11):
+        ptrs = [P] * 13
+        ptrs[i] = None
+        assert call(ptrs=tuple(ptrs)) == _lib.TA_ERR_INVALID_ARG, i
+    assert call(ws=None) == _lib.TA_ERR_WORKSPACE
+    assert call(ws_bytes=ws_need - 1) == _lib.TA_ERR_WORKSPACE
+    assert call(ws=P + 8) == _lib.TA_ERR_WORKSPACE

@@ -7,6 +7,7 @@ entry points keep the C names:
 * ``tree_attn_verify``   -- tree-masked attention over every draft node
 * ``tree_attn_expand``   -- the same for the w newest leaves (non-square mask)
 * ``accept_greedy_path`` -- greedy longest accepted path, AL and bonus token
+* ``accept_sampling_path`` -- the same by speculative sampling (temperature > 0)
 * ``tree_cache_reroot``  -- evolving-tree-cache re-root with in-place KV moves
 * ``tree_expand_top_w``  -- maximum-likelihood expansion: append the w best leaves
 * ``tree_rope_append``   -- RoPE at tree positions + KV append of the new nodes
@@ -22,6 +23,8 @@ from ._lib import (  # noqa: F401
     TreeAttnError,
     Workspace,
     accept_greedy_path,
+    accept_sampling_path,
+    accept_sampling_workspace_bytes,
     load_library,
     ta_last_error,
     ta_status_string,

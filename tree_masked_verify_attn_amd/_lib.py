@@ -31,6 +31,8 @@ EXPORTED_SYMBOLS = (
     "tree_attn_verify",
     "tree_attn_expand",
     "accept_greedy_path",
+    "accept_sampling_path",
+    "accept_sampling_workspace_bytes",
     "tree_cache_reroot",
     "tree_expand_top_w",
     "tree_expand_top_w_workspace_bytes",
@@ -98,6 +100,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.accept_greedy_path.argtypes = [vp, c_int, vp, vp, vp, vp, c_int, c_int, c_int, vp, vp,
                                            vp, vp]
         lib.accept_greedy_path.restype = c_int
+        lib.accept_sampling_path.argtypes = [vp, vp, c_int] + [vp] * 6 + [f32] + [c_int] * 3 + \
+            [vp] * 4 + [c_size, vp]
+        lib.accept_sampling_path.restype = c_int
+        lib.accept_sampling_workspace_bytes.argtypes = [c_int, c_int]
+        lib.accept_sampling_workspace_bytes.restype = c_size
         lib.tree_cache_reroot.argtypes = [ctypes.POINTER(ta_kv), c_int, vp, vp, vp, vp, vp, vp,
                                           c_int, c_int, c_int, c_int, c_int, vp]
         lib.tree_cache_reroot.restype = c_int
@@ -377,6 +384,67 @@ def accept_greedy_path(logits, parent, tok, n_nodes, root_tok, path=None, path_l
                                 tok.data_ptr(), n_nodes.data_ptr(), root_tok.data_ptr(), B, n_max,
                                 V, path.data_ptr(), path_len.data_ptr(), bonus.data_ptr(),
                                 _stream(stream))
+    _check(st)
+    return path, path_len, bonus
+
+
+def accept_sampling_workspace_bytes(B: int, n_max: int) -> int:
+    n = load_library().accept_sampling_workspace_bytes(B, n_max)
+    if n == ctypes.c_size_t(-1).value:
+        raise TreeAttnError(TA_ERR_INVALID_ARG, "invalid sizes for a sampling workspace query")
+    return int(n)
+
+
+def accept_sampling_path(target_logits, draft_logits, parent, tok, n_nodes, root_tok, u_accept,
+                         u_bonus, temperature: float, path=None, path_len=None, bonus=None,
+                         workspace=None, stream=None):
+    """Tree verification by speculative sampling; returns ``(path, path_len,
+    bonus)`` int32 tensors.  ``u_accept [B][n_max]`` and ``u_bonus [B]`` are
+    fp32 uniforms in [0, 1) drawn by the caller."""
+    torch = _torch()
+    lib = load_library()
+    _need(target_logits, "target_logits", ndim=3)
+    dev = target_logits.device
+    _need(draft_logits, "draft_logits", dtype=target_logits.dtype, ndim=3, device=dev)
+    _need(parent, "parent", dtype=torch.int32, ndim=2, device=dev)
+    _need(tok, "tok", dtype=torch.int32, ndim=2, device=dev)
+    _need(n_nodes, "n_nodes", dtype=torch.int32, ndim=1, device=dev)
+    _need(root_tok, "root_tok", dtype=torch.int32, ndim=1, device=dev)
+    _need(u_accept, "u_accept", dtype=torch.float32, ndim=2, device=dev)
+    _need(u_bonus, "u_bonus", dtype=torch.float32, ndim=1, device=dev)
+    B, n_max, V = (int(x) for x in target_logits.shape)
+    if tuple(draft_logits.shape) != (B, n_max, V):
+        raise ValueError("draft_logits must have target_logits' shape")
+    for t, name in ((parent, "parent"), (tok, "tok"), (u_accept, "u_accept")):
+        if tuple(t.shape) != (B, n_max):
+            raise ValueError(f"{name} must be [B][n_max] matching the logits")
+    if n_nodes.shape[0] != B or root_tok.shape[0] != B or u_bonus.shape[0] != B:
+        raise ValueError("n_nodes, root_tok and u_bonus must be [B]")
+    if path is None:
+        path = torch.empty((B, n_max), dtype=torch.int32, device=dev)
+    if path_len is None:
+        path_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    if bonus is None:
+        bonus = torch.empty((B,), dtype=torch.int32, device=dev)
+    _need(path, "path", dtype=torch.int32, ndim=2, device=dev)
+    _need(path_len, "path_len", dtype=torch.int32, ndim=1, device=dev)
+    _need(bonus, "bonus", dtype=torch.int32, ndim=1, device=dev)
+    if tuple(path.shape) != (B, n_max) or path_len.shape[0] != B or bonus.shape[0] != B:
+        raise ValueError("path must be [B][n_max], path_len and bonus [B]")
+    nbytes = accept_sampling_workspace_bytes(B, n_max)
+    if workspace is None:
+        ws = _workspace_for(dev, nbytes)
+    else:
+        ws = workspace.get(nbytes, dev) if isinstance(workspace, Workspace) else workspace
+    if ws is not None:
+        _need(ws, "workspace", device=dev)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = lib.accept_sampling_path(target_logits.data_ptr(), draft_logits.data_ptr(),
+                                  _dtype_code(target_logits), parent.data_ptr(), tok.data_ptr(),
+                                  n_nodes.data_ptr(), root_tok.data_ptr(), u_accept.data_ptr(),
+                                  u_bonus.data_ptr(), ctypes.c_float(float(temperature)), B,
+                                  n_max, V, path.data_ptr(), path_len.data_ptr(),
+                                  bonus.data_ptr(), _ptr(ws), ws_bytes, _stream(stream))
     _check(st)
     return path, path_len, bonus
 

@@ -296,6 +296,37 @@ int accept_greedy_path(const void* logits, int logit_dtype, const int32_t* paren
   return hip_status(e, "accept_greedy_path launch");
 }
 
+size_t accept_sampling_workspace_bytes(int B, int n_max) {
+  if (B < 0 || n_max < 1 || n_max > TA_MAX_NODES) return static_cast<size_t>(-1);
+  return ta::samp_ws_bytes(B, n_max);
+}
+
+int accept_sampling_path(const void* target_logits, const void* draft_logits, int logit_dtype,
+                         const int32_t* parent, const int32_t* tok, const int32_t* n_nodes,
+                         const int32_t* root_tok, const float* u_accept, const float* u_bonus,
+                         float temperature, int B, int n_max, int V, int32_t* path,
+                         int32_t* path_len, int32_t* bonus, void* ws, size_t ws_bytes,
+                         void* stream) {
+  if (B < 0 || n_max < 1 || V < 1) return TA_ERR_INVALID_ARG;
+  if (n_max > TA_MAX_NODES) return TA_ERR_TREE_TOO_LARGE;
+  if (logit_dtype != TA_F32 && logit_dtype != TA_BF16) return TA_ERR_UNSUPPORTED;
+  if (!(temperature > 0.f) || temperature == INFINITY) return TA_ERR_INVALID_ARG;
+  const float inv_t = 1.f / temperature;
+  if (!(inv_t > 0.f) || inv_t == INFINITY) return TA_ERR_INVALID_ARG;
+  if (target_logits == nullptr || draft_logits == nullptr || parent == nullptr ||
+      tok == nullptr || n_nodes == nullptr || root_tok == nullptr || u_accept == nullptr ||
+      u_bonus == nullptr || path == nullptr || path_len == nullptr || bonus == nullptr)
+    return TA_ERR_INVALID_ARG;
+  if (B == 0) return TA_OK;
+  if (ws == nullptr || ws_bytes < ta::samp_ws_bytes(B, n_max) || !aligned16(ws))
+    return TA_ERR_WORKSPACE;
+  hipError_t e = ta::launch_accept_sampling(target_logits, draft_logits, logit_dtype, parent, tok,
+                                            n_nodes, root_tok, u_accept, u_bonus, inv_t, B, n_max,
+                                            V, path, path_len, bonus, ws,
+                                            static_cast<hipStream_t>(stream));
+  return hip_status(e, "accept_sampling_path launch");
+}
+
 int tree_rope_append(const void* q, void* q_out, const void* k_new, const void* v_new, ta_kv kv,
                      const int32_t* prefix_len, const int32_t* parent, const int32_t* n_nodes,
                      int B, int n_q, int n_max, int expand, int Hq, int Hkv, int d, int dtype,
