@@ -247,6 +247,7 @@ class ChainVerify(_Workload):
         self.batch = _VerifyBatch(ta, up, c, ta.KVCache(up(c.k, True), up(c.v, True)),
                                   up(c.q, True))
         self._rope = None
+        self._samp = None
         self.config = {"workload": "chain_verify", "batch": c.B, "Hq": c.Hq, "Hkv": c.Hkv,
                        "head_dim": c.d, "prefix": int(c.prefix_len[0]), "D": c.n_max - 1,
                        "rows_per_kv_head": c.G * c.n_max, "vocab": c.vocab,
@@ -272,7 +273,27 @@ class ChainVerify(_Workload):
 
         def rope(i, ws, opts):
             bt.ta.tree_rope_append(bt.q, k_new, v_new, bt.kv, bt.P, bt.par, bt.n, q_out=q_out)
-        return {"rope_append": rope}
+
+        if self._samp is None:
+            # Sampling verification of the same trees at temperature 1: the
+            # draft's logits are the target's plus seeded Gaussian noise
+            # (sd 1), the uniforms seeded; outputs go to their own arrays.
+            g = torch.Generator(device=bt.logits.device).manual_seed(4242)
+            dft = (bt.logits.float() + torch.randn(bt.logits.shape, generator=g,
+                                                   device=bt.logits.device)).to(bt.logits.dtype)
+            u = torch.rand(bt.tok.shape, generator=g, device=bt.logits.device)
+            ub = torch.rand(bt.tok.shape[0], generator=g, device=bt.logits.device)
+            ws_s = torch.empty(bt.ta.accept_sampling_workspace_bytes(*bt.tok.shape),
+                               dtype=torch.uint8, device=bt.logits.device)
+            outs = (torch.empty_like(bt.path), torch.empty_like(bt.plen),
+                    torch.empty_like(bt.bonus))
+            self._samp = (dft, u, ub, ws_s, outs)
+        dft, u, ub, ws_s, outs = self._samp
+
+        def sampling(i, ws, opts):
+            bt.ta.accept_sampling_path(bt.logits, dft, bt.par, bt.tok, bt.n, bt.root_tok, u, ub,
+                                       1.0, *outs, workspace=ws_s)
+        return {"rope_append": rope, "accept_sampling": sampling}
 
     def attn_bytes(self, i):
         return self.batch.bytes

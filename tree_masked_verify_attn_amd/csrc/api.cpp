@@ -311,8 +311,9 @@ int accept_sampling_path(const void* target_logits, const void* draft_logits, in
   if (n_max > TA_MAX_NODES) return TA_ERR_TREE_TOO_LARGE;
   if (logit_dtype != TA_F32 && logit_dtype != TA_BF16) return TA_ERR_UNSUPPORTED;
   if (!(temperature > 0.f) || temperature == INFINITY) return TA_ERR_INVALID_ARG;
-  const float inv_t = 1.f / temperature;
-  if (!(inv_t > 0.f) || inv_t == INFINITY) return TA_ERR_INVALID_ARG;
+  // logits scale for the base-2 exponentials: log2(e) / T
+  const float c2 = static_cast<float>(1.4426950408889634 / static_cast<double>(temperature));
+  if (!(c2 > 0.f) || c2 == INFINITY) return TA_ERR_INVALID_ARG;
   if (target_logits == nullptr || draft_logits == nullptr || parent == nullptr ||
       tok == nullptr || n_nodes == nullptr || root_tok == nullptr || u_accept == nullptr ||
       u_bonus == nullptr || path == nullptr || path_len == nullptr || bonus == nullptr)
@@ -321,7 +322,7 @@ int accept_sampling_path(const void* target_logits, const void* draft_logits, in
   if (ws == nullptr || ws_bytes < ta::samp_ws_bytes(B, n_max) || !aligned16(ws))
     return TA_ERR_WORKSPACE;
   hipError_t e = ta::launch_accept_sampling(target_logits, draft_logits, logit_dtype, parent, tok,
-                                            n_nodes, root_tok, u_accept, u_bonus, inv_t, B, n_max,
+                                            n_nodes, root_tok, u_accept, u_bonus, c2, B, n_max,
                                             V, path, path_len, bonus, ws,
                                             static_cast<hipStream_t>(stream));
   return hip_status(e, "accept_sampling_path launch");

@@ -98,7 +98,7 @@ size_t samp_ws_bytes(int B, int n_max);
 hipError_t launch_accept_sampling(const void* tgt, const void* dft, int logit_dtype,
                                   const int32_t* parent, const int32_t* tok,
                                   const int32_t* n_nodes, const int32_t* root_tok,
-                                  const float* u_accept, const float* u_bonus, float inv_t, int B,
+                                  const float* u_accept, const float* u_bonus, float c2, int B,
                                   int n_max, int V, int32_t* path, int32_t* path_len,
                                   int32_t* bonus, void* ws, hipStream_t s);
 size_t topw_ws_bytes(int B, int n_max, int w);
