@@ -49,8 +49,24 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=[f"seed{c[0]}" for c in CASES])
-def test_rope_append_matches_oracle(ta, case):
+def _unaligned(t):
+    """A copy of t whose data starts one element past a 16-byte boundary."""
+    import torch
+    flat = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+    view = flat[1:].view(t.shape)
+    view.copy_(t)
+    return view
+
+
+MODES = [(CASES[0], "plain"), (CASES[1], "plain"), (CASES[2], "plain"), (CASES[3], "plain"),
+         (CASES[4], "plain"), (CASES[1], "unaligned"), (CASES[2], "unaligned"),
+         (CASES[3], "in_place")]
+
+
+@pytest.mark.parametrize("case,mode", MODES, ids=[f"seed{c[0]}-{m}" for c, m in MODES])
+def test_rope_append_matches_oracle(ta, case, mode):
+    """Aligned rows take the 16-byte vector kernel; an input one element off a
+    16-byte boundary takes the element-wise one; in place, q_out is q."""
     import torch
     seed, B, Hq, Hkv, d, P_range, n_max, dtype, paged, w = case
     c = random_case(seed, B, Hq, Hkv, d, P_range=P_range, n_max=n_max, dtype=dtype, paged=paged)
@@ -67,8 +83,13 @@ def test_rope_append_matches_oracle(ta, case):
     dc = DevCase(c)
     k_before = to_f64(dc.k)
     dq, dk, dv = dev_tensor(q, dtype), dev_tensor(kn, dtype), dev_tensor(vn, dtype)
+    if mode == "unaligned":
+        dq = _unaligned(dq)
+        assert dq.data_ptr() % 16 != 0
     qo = ta.tree_rope_append(dq, dk, dv, dc.kv, dc.prefix_len, dc.parent, dc.n_nodes, base=BASE,
-                             expand=bool(w))
+                             expand=bool(w), q_out=dq if mode == "in_place" else None)
+    if mode == "in_place":
+        assert qo.data_ptr() == dq.data_ptr()
     torch.cuda.synchronize()
     qo, k_after, v_after = to_f64(qo), to_f64(dc.k), to_f64(dc.v)
     q_ref, rows = oracle.rope_append(_f64(q, dtype), _f64(kn, dtype), _f64(vn, dtype),

@@ -80,7 +80,7 @@ constexpr int kStreamMaxSplitBlocks = 512;  // paged: block ids of one split hel
 // Units kernel: every (sequence, row tile, KV head) job's tiles laid end to end,
 // G equal ranges of them, one per work group; then a combine launch.
 constexpr int kUnitMaxSeqs = 1024;
-constexpr int kUnitJobCost = 2;  // stream units a job counts beyond its tiles
+constexpr int kUnitJobCost = 6;  // stream units a job counts beyond its tiles
 hipError_t launch_attn_units(const AttnParams& p, hipStream_t s);
 hipError_t launch_attn_merge_units(const AttnParams& p, hipStream_t s);
 
