@@ -644,7 +644,7 @@ def main(argv=None):
     a = ap.parse_args(argv)
 
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the verify kernel shards by (sequence, KV head) with no exchange; "
               "run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
@@ -683,6 +683,7 @@ def main(argv=None):
     torch.cuda.synchronize()
     w.check()   # correctness guard for the timed configuration
     steps = range(a.warmup, a.warmup + a.steps)
+    extra_ms = {}  # calls timed beside the step (graph mode only)
 
     if a.eager:
         # one Python call per entry point: host launch cost is inside the steps
@@ -720,7 +721,6 @@ def main(argv=None):
         ms_per_step = start.elapsed_time(stop) / a.steps
         w.check()
         phase_ms = []
-        extra_ms = {}
         for j in range(nph):
             g = capture(lambda: [w.phase(i, j, ws, opts) for i in steps])
             g.replay()
