@@ -113,6 +113,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_units_kernel(AttnParams p) {
   __shared__ USeg sSeg[kMaxSeg];
   __shared__ uint64_t sRowMask[kMaxTreeSeg][RPT][kMaskWords];
   __shared__ int sScan[kThreads / 64];
+  __shared__ int sSimd[4];
   __shared__ int sNumSeg, sBatchTiles, sNext;
 
   const int g = blockIdx.x;
@@ -122,9 +123,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_units_kernel(AttnParams p) {
   const int wave = tid >> 6;
   const int lhi = lane >> 5;
   const int l32 = lane & 31;
-  const int rg = wave < NRG ? wave : -1;           // computing waves own a 32-row group
-  const bool loader = wave >= 4 - kDmaWaves;        // waves that issue ring loads
-  const int dma_rank = wave - (4 - kDmaWaves);      // index among the loading waves
+  const int role = wave_role(wave, g, p.cu_count, sSimd);
+  const int rg = role < NRG ? role : -1;           // computing waves own a 32-row group
+  const bool loader = role >= 4 - kDmaWaves;        // waves that issue ring loads
+  const int dma_rank = role - (4 - kDmaWaves);      // index among the loading waves
   const int row_in_tile = (rg < 0 ? 0 : rg) * 32 + l32;
   const int B = p.B;
   const int bs = p.block_size;
