@@ -196,6 +196,32 @@ def test_split_count_invariance(ta):
             assert np.nanmax(np.abs(O - ref[0])) < 4e-3 and np.nanmax(np.abs(L - ref[1])) < 1e-4
 
 
+@pytest.mark.parametrize("kernel", [3, 4])
+def test_combine_ignores_stale_workspace(ta, kernel):
+    """The combine launch fetches its first partial states before it knows a
+    sequence's split count; slots past a short sequence's last split hold
+    whatever an earlier call left (here NaN bytes) and must not reach the
+    result."""
+    import torch
+    c = random_case(94, 6, 16, 2, 128, P_range=(40, 3000), n_max=8, dtype="bf16",
+                    target_side=True, paged=kernel == 4)
+    dc = DevCase(c)
+    ws = ta.Workspace()
+    for rep in range(2):
+        out = torch.full_like(dc.q, float("nan"))
+        lse = torch.full((c.B, c.Hq, c.n_max), float("nan"), dtype=torch.float32,
+                         device=dc.q.device)
+        ta.tree_attn_verify(dc.q, dc.kv, dc.prefix_len, dc.parent, dc.n_nodes, c.scale, out=out,
+                            lse=lse, workspace=ws, chunk_tokens=64, kernel=kernel)
+        torch.cuda.synchronize()
+        if rep == 0:
+            ws.buf.view(torch.float32)[: ws.buf.numel() // 4].fill_(float("nan"))
+            torch.cuda.synchronize()
+    Or, Lr = oracle.verify(c)
+    assert_attn_close(to_f64(out), lse.cpu().numpy().astype(np.float64), Or, Lr, "bf16",
+                      what=f"stale workspace kernel{kernel}")
+
+
 def test_repeated_calls_are_deterministic_and_reset_counters(ta):
     c = random_case(78, 3, 8, 2, 128, P_range=(300, 900), n_max=16, dtype="bf16")
     dc = DevCase(c)

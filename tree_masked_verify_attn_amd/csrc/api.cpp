@@ -201,7 +201,6 @@ int run_attention(const void* q, ta_kv kv, const int32_t* prefix_len, const int3
   p.expand = expand;
   p.scale_log2 = scale * 1.4426950408889634f;
   p.chunk = pl.chunk;
-  p.cu_count = device_cu_count();
   p.n_split = pl.n_split;
   p.rows_per_tile = pl.rows_per_tile;
   p.n_row_tiles = pl.n_row_tiles;

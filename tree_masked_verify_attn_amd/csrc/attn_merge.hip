@@ -41,10 +41,6 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(AttnParams p) {
   const int bh = blockIdx.x;
   const int b = bh / p.Hkv;
   const int hkv = bh % p.Hkv;
-  SeqBounds sb;
-  if (!seq_bounds(p.prefix_len, p.n_nodes, b, p.n_max, p.T_cap, sb)) return;
-  const int nsplit = (sb.T + p.chunk - 1) / p.chunk;
-  if (nsplit <= 1) return;  // the attention kernel wrote this sequence's results
   const int groups = p.d / 4;
   const int per_tile = p.rows_per_tile * groups;
   const int e = blockIdx.y * kThreads + threadIdx.x;
@@ -52,6 +48,31 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(AttnParams p) {
   if (rtile >= p.n_row_tiles) return;
   const int r = (e % per_tile) / groups;
   const int dg = e % groups;
+  const size_t part = static_cast<size_t>(bh * p.n_row_tiles + rtile) * p.n_split;
+  // Partial states are read kBatch at a time with unconditional loads (splits
+  // past the last repeat one and get weight zero), so that a batch's loads are
+  // all in flight before the first is used; batches combine online.  The
+  // first batch does not wait for the sequence's length: its slots exist for
+  // every plan (clamped to the allocated splits), and the slots past the
+  // sequence's last split are discarded below.
+  float ms[kBatch], ls[kBatch];
+  f32x4 os[kBatch];
+  auto load_batch = [&](int s0, int last) {
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int sp = s0 + k < last ? s0 + k : last;
+      const size_t pr = (part + sp) * p.rows_per_tile + r;
+      const float2 ml = *reinterpret_cast<const float2*>(p.ws_ml + pr * 2);
+      ms[k] = ml.x;
+      ls[k] = ml.y;
+      os[k] = *reinterpret_cast<const f32x4*>(p.ws_o + pr * p.d + 4 * dg);
+    }
+  };
+  load_batch(0, p.n_split - 1);
+  SeqBounds sb;
+  if (!seq_bounds(p.prefix_len, p.n_nodes, b, p.n_max, p.T_cap, sb)) return;
+  const int nsplit = (sb.T + p.chunk - 1) / p.chunk;
+  if (nsplit <= 1) return;  // the attention kernel wrote this sequence's results
   const int gr = rtile * p.rows_per_tile + r;
   const int R = p.n_q * p.G;
   if (gr >= R) return;
@@ -59,27 +80,17 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(AttnParams p) {
   const int node = p.expand ? sb.n - p.n_q + slot : slot;
   if (node < 0 || node >= sb.n) return;
 
-  const size_t part = static_cast<size_t>(bh * p.n_row_tiles + rtile) * p.n_split;
-  // Partial states are read kBatch at a time with unconditional loads (splits
-  // past the last repeat it and get weight zero), so that a batch's loads are
-  // all in flight before the first is used; batches combine online.
   float M = -INFINITY, L = 0.f;
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < nsplit; s0 += kBatch) {
-    float ms[kBatch], ls[kBatch];
-    f32x4 os[kBatch];
-#pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      const int sp = s0 + k < nsplit ? s0 + k : nsplit - 1;
-      const size_t pr = (part + sp) * p.rows_per_tile + r;
-      const float2 ml = *reinterpret_cast<const float2*>(p.ws_ml + pr * 2);
-      ms[k] = ml.x;
-      ls[k] = ml.y;
-      os[k] = *reinterpret_cast<const f32x4*>(p.ws_o + pr * p.d + 4 * dg);
-    }
+    if (s0 > 0) load_batch(s0, nsplit - 1);
 #pragma unroll
     for (int k = 0; k < kBatch; ++k)
-      if (s0 + k >= nsplit) ms[k] = -INFINITY;
+      if (s0 + k >= nsplit) {  // not a split of this sequence (may hold stale bytes)
+        ms[k] = -INFINITY;
+        ls[k] = 0.f;
+        os[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
     float Mb = M;
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) Mb = fmaxf(Mb, ms[k]);

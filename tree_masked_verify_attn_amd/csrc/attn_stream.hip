@@ -56,9 +56,7 @@ __global__ __launch_bounds__(kThreads, S == 3 ? 3 : 2) void attn_stream_kernel(A
   const int t_begin = split * p.chunk;
   const int t_end = min(sb.T, t_begin + p.chunk);
 
-  __shared__ int sSimd[4];
-  const int role = wave_role(wave, bh + gridDim.x * (split + gridDim.y * rtile), p.cu_count, sSimd);
-  const int rg = role < NRG ? role : -1;  // computing waves own one 32-row group each
+  const int rg = wave < NRG ? wave : -1;  // computing waves own one 32-row group each
   const int R = p.n_q * p.G;
   const int row_in_tile = (rg < 0 ? 0 : rg) * 32 + l32;
   const int grow = rtile * C::RPT + row_in_tile;

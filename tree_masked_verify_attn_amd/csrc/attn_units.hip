@@ -113,7 +113,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_units_kernel(AttnParams p) {
   __shared__ USeg sSeg[kMaxSeg];
   __shared__ uint64_t sRowMask[kMaxTreeSeg][RPT][kMaskWords];
   __shared__ int sScan[kThreads / 64];
-  __shared__ int sSimd[4];
   __shared__ int sNumSeg, sBatchTiles, sNext;
 
   const int g = blockIdx.x;
@@ -123,10 +122,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_units_kernel(AttnParams p) {
   const int wave = tid >> 6;
   const int lhi = lane >> 5;
   const int l32 = lane & 31;
-  const int role = wave_role(wave, g, p.cu_count, sSimd);
-  const int rg = role < NRG ? role : -1;           // computing waves own a 32-row group
-  const bool loader = role >= 4 - kDmaWaves;        // waves that issue ring loads
-  const int dma_rank = role - (4 - kDmaWaves);      // index among the loading waves
+  const int rg = wave < NRG ? wave : -1;           // computing waves own a 32-row group
+  const bool loader = wave >= 4 - kDmaWaves;        // waves that issue ring loads
+  const int dma_rank = wave - (4 - kDmaWaves);      // index among the loading waves
   const int row_in_tile = (rg < 0 ? 0 : rg) * 32 + l32;
   const int B = p.B;
   const int bs = p.block_size;
@@ -672,6 +670,9 @@ __global__ __launch_bounds__(kThreads) void merge_units_kernel(AttnParams p) {
   const int bh = blockIdx.x;
   const int b = bh / p.Hkv;
   const int hkv = bh % p.Hkv;
+  // the stream starts load alongside the sequence's lengths
+  const int Sh = p.ws_seq[p.B];  // stream units per KV head
+  const int seq0 = p.ws_seq[b];
   const SeqJobs s = seq_jobs(p, b, RPT);
   if (s.rts == 0) return;
   const int groups = p.d / 4;
@@ -687,11 +688,10 @@ __global__ __launch_bounds__(kThreads) void merge_units_kernel(AttnParams p) {
   const int node = p.expand ? s.n - p.n_q + slot : slot;
   if (node < 0 || node >= s.n) return;
 
-  const int Sh = p.ws_seq[p.B];  // stream units per KV head
   const int N = Sh * p.Hkv;
   const int G = p.n_split;  // work groups of the attention launch
   const int U = (N + G - 1) / G;
-  const int J0 = hkv * Sh + p.ws_seq[b] + (rtile - s.rt_lo) * (s.tiles + kJobCost);
+  const int J0 = hkv * Sh + seq0 + (rtile - s.rt_lo) * (s.tiles + kJobCost);
   const int J1 = J0 + s.tiles;  // the job's tiles (its cost units follow)
   const int g0 = J0 / U, g1 = (J1 - 1) / U;
   if (g0 == g1) return;  // one group held the whole job and wrote its rows

@@ -57,27 +57,6 @@ __device__ __forceinline__ void raw_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
 }
 
-// Role of this wave in its work group: roles 0 .. NRG-1 compute a 32-row
-// group, the others only load (or idle).  A CU has four SIMDs, and the
-// hardware places the four waves of a group on them in a rotating order, so
-// the waves with equal indices of the two groups sharing a CU may sit on one
-// SIMD, which then carries two computing waves while another only loads.
-// When the group's waves are on four distinct SIMDs the role follows the
-// SIMD instead: the group in a CU's first slot computes on SIMDs 0, 1, ..,
-// the one in its second slot on SIMDs 2, 3, ..  The dispatcher fills one slot
-// of every CU before the second, so the slot is taken to be the parity of
-// (linear group id / compute units).  A wrong guess only costs speed: the
-// roles are always a permutation of the wave indices.  Ends with a barrier.
-__device__ __forceinline__ int wave_role(int wave, int linear_group, int cu_count, int* sSimd4) {
-  // HW_ID (hardware register 4) bits 5:4 = the SIMD of this wave
-  if ((threadIdx.x & 63) == 0) sSimd4[wave] = (__builtin_amdgcn_s_getreg((31 << 11) | 4) >> 4) & 3;
-  __syncthreads();
-  const int s0 = sSimd4[0], s1 = sSimd4[1], s2 = sSimd4[2], s3 = sSimd4[3];
-  if (((1 << s0) | (1 << s1) | (1 << s2) | (1 << s3)) != 15 || cu_count <= 0) return wave;
-  const int first = ((linear_group / cu_count) & 1) ? 2 : 0;
-  return (sSimd4[wave] - first) & 3;
-}
-
 template <int D, int NRG, int S>
 struct SCfg {
   static constexpr int CH = D / 8;                  // 16-byte chunks per row

@@ -64,7 +64,6 @@ struct AttnParams {
   // hold 2G slots of rows_per_tile rows, ws_seq the stream start of every
   // sequence and the stream's length (B + 1 entries)
   int32_t* ws_seq;
-  int32_t cu_count;     // compute units of the device (wave roles, see wave_role)
 };
 
 // Workspace layout: the partial outputs, then the (max, sum) pairs.  Returns
