@@ -202,11 +202,13 @@ def test_topw_large_vocab(ta, V, dtype):
     _check_round(par[0], tk[0], cum[0], n, lg_used[0], 3, n_max, par1[0], tok1[0], cum1[0], int(n1[0]))
 
 
-@pytest.mark.parametrize("V,w,dtype", [(1000, 8, "f32"), (4096, 16, "bf16"), (777, 5, "f32")])
+@pytest.mark.parametrize("V,w,dtype", [(1000, 8, "f32"), (4096, 16, "bf16"), (777, 5, "f32"),
+                                     (20000, 8, "f32"), (40000, 16, "bf16")])
 def test_topw_all_ties(ta, V, w, dtype):
     """Every logit equal: every thread's best logit ties, so the threshold
     step ranks hundreds of keys; the picks are the root's lowest free tokens
-    in token order (equal scores: lower parent, then lower token)."""
+    in token order (equal scores: lower parent, then lower token), also for
+    vocabularies of tens of thousands of tied logits."""
     n_max, n = 30, 6
     parent = np.array([-1, -1, 0, 0, 1, -1] + [-1] * (n_max - 6), np.int32)[None]
     tok = np.array([0, 2, 0, 1, 5, 3] + [0] * (n_max - 6), np.int32)[None]
