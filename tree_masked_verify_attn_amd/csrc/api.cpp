@@ -230,7 +230,7 @@ int run_attention(const void* q, ta_kv kv, const int32_t* prefix_len, const int3
     return hip_status(e, where);
   }
   if (pl.kernel == 3) {
-    e = ta::launch_attn_stream(p, 4, s);
+    e = ta::launch_attn_stream(p, s);
     where = "attention (streaming MFMA kernel) launch";
   } else if (pl.kernel == 2) {
     e = ta::launch_attn_mfma(p, s);

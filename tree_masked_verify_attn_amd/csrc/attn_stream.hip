@@ -11,8 +11,9 @@
 //    base + 16 * i of the XOR-swizzled layout.
 //  * The loads are issued from inline assembly and waited for with explicit
 //    s_waitcnt vmcnt(N) + s_barrier, so the compiler cannot add a blanket
-//    vmcnt(0) in front of every LDS read: S-1 stages stay in flight while one
-//    is consumed.
+//    vmcnt(0) in front of every LDS read: S-2 stages stay in flight while two
+//    are read (a tile's P.V and the next tile's scores run in the same
+//    step).
 //  * Each computing wave owns one 32-row group of the tile's rows and
 //    consumes every stage; waves beyond the row groups only issue loads.
 //  * Paged caches: the split's block ids are copied to LDS first, so the
@@ -24,10 +25,11 @@
 namespace ta {
 namespace {
 
-// S = 4: 64 KiB ring, two work groups per compute unit.  S = 3: 48 KiB ring and
-// registers capped for three work groups per compute unit.
+// S = 4: a 64 KiB ring, two work groups per compute unit.  (A three-stage
+// ring for three groups per CU does not fit: 128 query rows need the
+// registers of two.)
 template <int D, int NRG, int S>
-__global__ __launch_bounds__(kThreads, S == 3 ? 3 : 2) void attn_stream_kernel(AttnParams p) {
+__global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) {
   using C = SCfg<D, NRG, S>;
   static_assert(S >= 2 && S <= 4, "ring depth");
   __shared__ __attribute__((aligned(1024))) uint8_t sRing[C::LDS];
@@ -381,9 +383,9 @@ hipError_t launch_ds(const AttnParams& p, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_attn_stream(const AttnParams& p, int stages, hipStream_t s) {
-  if (p.d == 128) return stages == 3 ? launch_ds<128, 3>(p, s) : launch_ds<128, 4>(p, s);
-  if (p.d == 64) return stages == 3 ? launch_ds<64, 3>(p, s) : launch_ds<64, 4>(p, s);
+hipError_t launch_attn_stream(const AttnParams& p, hipStream_t s) {
+  if (p.d == 128) return launch_ds<128, 4>(p, s);
+  if (p.d == 64) return launch_ds<64, 4>(p, s);
   return hipErrorInvalidValue;
 }
 

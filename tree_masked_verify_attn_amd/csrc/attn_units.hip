@@ -354,7 +354,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_units_kernel(AttnParams p) {
     // ---- segment state ----
     // compute side: the segment of the tile being consumed
     int kc = 0;
-    int c_j1, c_tb0, c_te, c_P, c_tree, c_flags, c_b, c_rtile, c_hkv;
+    int c_j1, c_tb0, c_te, c_P, c_tree, c_flags, c_b, c_hkv;
     auto load_c = [&](int k) {
       c_j1 = __builtin_amdgcn_readfirstlane(sSeg[k].j1);
       c_tb0 = __builtin_amdgcn_readfirstlane(sSeg[k].t_begin - sSeg[k].j0 * kTile);
@@ -363,7 +363,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_units_kernel(AttnParams p) {
       c_tree = __builtin_amdgcn_readfirstlane(sSeg[k].tree);
       c_flags = __builtin_amdgcn_readfirstlane(sSeg[k].flags);
       c_b = __builtin_amdgcn_readfirstlane(sSeg[k].b);
-      c_rtile = __builtin_amdgcn_readfirstlane(sSeg[k].rtile);
       c_hkv = __builtin_amdgcn_readfirstlane(sSeg[k].hkv);
     };
     // issue side: the segment of the next stage to load
@@ -611,7 +610,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_units_kernel(AttnParams p) {
       const int jend = next ? j1 - 1 : j1;  // with a next segment its last tile is peeled
       f32x16 s_cur = rg >= 0 ? qk(j0 & (kS - 1)) : f32x16{};
       int jj = j0;
-#pragma unroll 4
       for (; jj < min(jc, jend); ++jj) {
         if (jj + 1 < L) arrive(jj + 1, (jj + 1) & (kS - 1));
         if (rg >= 0) {

@@ -74,8 +74,8 @@ hipError_t launch_attn_generic(const AttnParams& p, int dtype, hipStream_t s);
 // Second launch of a split call: combines the partial states into out / lse.
 hipError_t launch_attn_merge(const AttnParams& p, int dtype, hipStream_t s);
 hipError_t launch_attn_mfma(const AttnParams& p, hipStream_t s);
-// Streaming MFMA variant: `stages` (3 or 4) 32-position LDS stages in flight.
-hipError_t launch_attn_stream(const AttnParams& p, int stages, hipStream_t s);
+// Streaming MFMA variant: a ring of four 32-position LDS stages.
+hipError_t launch_attn_stream(const AttnParams& p, hipStream_t s);
 constexpr int kStreamMaxSplitBlocks = 512;  // paged: block ids of one split held in LDS
 // Units kernel: every (sequence, row tile, KV head) job's tiles laid end to end,
 // G equal ranges of them, one per work group; then a combine launch.
