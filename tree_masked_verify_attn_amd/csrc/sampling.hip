@@ -115,7 +115,7 @@ __device__ __forceinline__ void row_lse(const void* row, int V, float c2, float&
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const int j = base + u * kThreads + tid;
-        w[u] = x4[j < nv ? j : nv - 1];
+        w[u] = __builtin_nontemporal_load(x4 + (j < nv ? j : nv - 1));  // read once: streaming policy
       }
       float z[kUnroll * kPer];
 #pragma unroll
