@@ -163,19 +163,21 @@ def test_units_kernel_mixed_lengths(ta, seed):
 @pytest.mark.parametrize("case", [
     # (seed, B, Hq, Hkv, d, P_range, n_max, block_size)
     (92, 8, 64, 8, 128, (3500, 4500), 6, 1),   # 1-position blocks: ranges set up in batches
-    (93, 6, 16, 2, 64, (0, 3000), 8, 16),      # 64 rows, d = 64: split loads, 4 KiB halves
-], ids=["many-batches", "d64"])
-def test_units_kernel_split_loads(ta, case):
-    """Units kernel with at most two row groups: one wave loads K by DMA, one
-    loads V through registers; ranges needing several set-up batches."""
+    (93, 6, 16, 2, 64, (0, 3000), 8, 16),      # 64 rows, d = 64: 4 KiB ring halves
+    (95, 3, 4, 2, 128, (0, 2000), 256, 16),    # maximum tree: 512 rows, four 128-row tiles
+], ids=["many-batches", "d64", "max-tree"])
+def test_units_kernel_batches_and_shapes(ta, case):
+    """Units kernel on ranges that need several set-up batches (1-position
+    blocks), 64-dimensional heads, and the maximum tree (256 nodes, whose
+    tree pieces fill the row-mask table in several batches)."""
     seed, B, Hq, Hkv, d, P_range, n_max, bsz = case
     c = random_case(seed, B, Hq, Hkv, d, P_range=P_range, n_max=n_max, dtype="bf16",
                     target_side=True, paged=True, block_size=bsz)
-    print(f"case seed={seed} units split loads d={d} block_size={bsz}", flush=True)
+    print(f"case seed={seed} units kernel d={d} n_max={n_max} block_size={bsz}", flush=True)
     dc = DevCase(c)
     O, L = _run_verify(ta, dc, 0, 4)
     Or, Lr = oracle.verify(c)
-    assert_attn_close(O, L, Or, Lr, "bf16", what=f"units split loads seed{seed}")
+    assert_attn_close(O, L, Or, Lr, "bf16", what=f"units kernel seed{seed}")
     _check_unwritten(O, L, c, lambda n: range(c.n_max))
 
 
