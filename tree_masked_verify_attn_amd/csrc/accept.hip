@@ -124,20 +124,27 @@ __global__ __launch_bounds__(kThreads) void accept_path_kernel(const int32_t* pa
   __shared__ unsigned long long sKey[kThreads / 64];
   const int b = blockIdx.x;
   const int i = threadIdx.x;
-  int n = n_nodes[b];
-  n = n < 0 ? 0 : (n > n_max ? n_max : n);
   const int32_t* par_b = parent + static_cast<size_t>(b) * n_max;
   int32_t* path_b = path + static_cast<size_t>(b) * n_max;
+  // every global load first (slot index clamped), so the launch pays one
+  // memory latency: the node count, root token, and this slot's argmax
+  // (parked by the first launch), parent and token
+  const int ic = i < n_max ? i : n_max - 1;
+  int n = n_nodes[b];
   const int rt = root_tok[b];
+  const int a_i = path_b[ic];
+  const int par_i = par_b[ic];
+  const int tok_i = tok[static_cast<size_t>(b) * n_max + ic];
+  n = n < 0 ? 0 : (n > n_max ? n_max : n);
 
-  if (i < n) sA[i] = path_b[i];  // argmax parked by the first launch
+  if (i < n) sA[i] = a_i;
   if (i < kMaskWords) sAcc[i] = 0;
-  build_ancestor_masks(par_b, n, sAnc, sJump);  // synchronises (also after the reads above)
+  build_ancestor_masks_of(par_i, n, sAnc, sJump);  // synchronises (also after the writes above)
 
   bool acc = false;
   if (i < n) {
-    const int p = clamp_parent(par_b[i], i);
-    acc = tok[static_cast<size_t>(b) * n_max + i] == (p < 0 ? rt : sA[p]);
+    const int p = clamp_parent(par_i, i);
+    acc = tok_i == (p < 0 ? rt : sA[p]);
   }
   const unsigned long long bal = __ballot(acc);  // 64 nodes per wave -> mask word (i >> 6)
   if ((i & 63) == 0) sAcc[i >> 6] = bal;

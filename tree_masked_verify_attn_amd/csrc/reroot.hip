@@ -36,21 +36,26 @@ __device__ __forceinline__ Plan make_plan(const int32_t* prefix_len, const int32
                                           uint64_t* sKept, int* sPath) {
   Plan pl;
   const int tid = threadIdx.x;
+  // every global load first (slot index clamped), so the plan pays one
+  // memory latency: the sequence's sizes and flag, this slot's path entry
+  // and parent
+  const int ic = tid < n_max ? tid : n_max - 1;
   int n = n_nodes[b];
-  n = n < 0 ? 0 : (n > n_max ? n_max : n);
   int k = path_len[b];
+  const int P = prefix_len[b];
+  const int kp = keep[b];
+  const int v_i = path[static_cast<size_t>(b) * n_max + ic];
+  const int par_i = parent[static_cast<size_t>(b) * n_max + ic];
+  n = n < 0 ? 0 : (n > n_max ? n_max : n);
   k = k < 0 ? 0 : (k > n ? n : k);
-  pl.P = prefix_len[b];
+  pl.P = P;
   pl.n = n;
   pl.k = k;
-  pl.keep = keep[b] != 0;
+  pl.keep = kp != 0;
   pl.valid = pl.P >= 0;
-  if (tid < k) {
-    int v = path[static_cast<size_t>(b) * n_max + tid];
-    sPath[tid] = v < 0 ? 0 : (v >= n ? n - 1 : v);
-  }
+  if (tid < k) sPath[tid] = v_i < 0 ? 0 : (v_i >= n ? n - 1 : v_i);
   if (tid < kMaskWords) sKept[tid] = 0;
-  build_ancestor_masks(parent + static_cast<size_t>(b) * n_max, n, sAnc, sJump);
+  build_ancestor_masks_of(par_i, n, sAnc, sJump);
   pl.v_last = k > 0 ? sPath[k - 1] : -1;
   bool kept = false;
   if (pl.keep && k > 0 && tid < n && tid != pl.v_last) kept = mask_bit(sAnc[tid], pl.v_last);

@@ -74,16 +74,18 @@ __device__ __forceinline__ int clamp_parent(int p, int i) { return (p >= -1 && p
 // anc[i] gets bit j set iff j == i or j is an ancestor of i.  After round k
 // each mask covers ancestors up to distance 2^k - 1, so 8 rounds reach any
 // depth below 256; the loop stops once every jump pointer has left the tree.
-// All threads of the block must call this (it synchronises).
+// All threads of the block must call this (it synchronises).  par_i is this
+// thread's parent entry (read only when threadIdx.x < n), so that callers can
+// load it together with their other inputs.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void build_ancestor_masks(const int32_t* parent_b, int n,
-                                                     uint64_t (*anc)[kMaskWords], int* jump) {
+__device__ __forceinline__ void build_ancestor_masks_of(int par_i, int n,
+                                                        uint64_t (*anc)[kMaskWords], int* jump) {
   const int i = threadIdx.x;
   uint64_t a[kMaskWords] = {0, 0, 0, 0};
   int j = -1;
   if (i < n) {
     a[i >> 6] = 1ull << (i & 63);
-    j = clamp_parent(parent_b[i], i);
+    j = clamp_parent(par_i, i);
 #pragma unroll
     for (int w = 0; w < kMaskWords; ++w) anc[i][w] = a[w];
     jump[i] = j;
@@ -105,6 +107,10 @@ __device__ __forceinline__ void build_ancestor_masks(const int32_t* parent_b, in
     j = jn;
     live = __syncthreads_or(j >= 0);
   }
+}
+__device__ __forceinline__ void build_ancestor_masks(const int32_t* parent_b, int n,
+                                                     uint64_t (*anc)[kMaskWords], int* jump) {
+  build_ancestor_masks_of(threadIdx.x < n ? parent_b[threadIdx.x] : -1, n, anc, jump);
 }
 
 __device__ __forceinline__ bool mask_bit(const uint64_t* m, int j) {
