@@ -95,3 +95,46 @@ def test_expand_workload_rounds_are_well_formed():
         n += c.w
         assert oracle.is_valid_parent(par, n)
     assert n == c.n_max
+
+
+def test_cumulative_scores_hand_example():
+    """A node's weight adds the log-probability of its token under its
+    PARENT's distribution (SwiftSpec summary, Section 3.1.3, maximum-likelihood
+    expansion).  Every row is a different distribution, written as the logs of
+    hand-picked probabilities, so reading a node's own row, a sibling's row or
+    the wrong token gives a different number."""
+    root = np.log([0.5, 0.25, 0.25])
+    rows = np.log([[0.1, 0.6, 0.3],     # after node 0
+                   [0.2, 0.2, 0.6],     # after node 1
+                   [0.7, 0.2, 0.1],     # after node 2
+                   [0.05, 0.9, 0.05]])  # after node 3
+    par = np.array([-1, 0, 1, 0], dtype=np.int32)
+    tok = np.array([1, 2, 0, 0], dtype=np.int32)
+    cum = oracle.cumulative_scores(par, tok, root, rows, 4)
+    # node 0: root's p(1) = 0.25; node 1: then node 0's p(2) = 0.3;
+    # node 2: then node 1's p(0) = 0.2; node 3 (node 0's child): node 0's p(0) = 0.1
+    expect = np.log([0.25, 0.25 * 0.3, 0.25 * 0.3 * 0.2, 0.25 * 0.1])
+    np.testing.assert_allclose(cum, expect, rtol=1e-14, atol=1e-14)
+    # unnormalised rows give the same weights (the log-softmax normalises)
+    cum2 = oracle.cumulative_scores(par, tok, root + 2.0, rows - 1.5, 4)
+    np.testing.assert_allclose(cum2, expect, rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_grown_tree_weights_equal_selection_scores(seed):
+    """The score select_top_w reports for a new leaf is the weight that leaf
+    has in the grown tree: cumulative_scores of the tree with the picks
+    appended reproduces it (the two functions compute the same definition
+    from different ends: per candidate, and per node of the result)."""
+    rng = np.random.default_rng(40 + seed)
+    vocab, n, w = 9, int(rng.integers(1, 7)), 5
+    par, tok = _tree(rng, n, vocab)
+    root = rng.standard_normal(vocab) * 2.0
+    rows = rng.standard_normal((n + w, vocab)) * 2.0
+    cum = oracle.cumulative_scores(par, tok, root, rows, n)
+    p, t, s = oracle.select_top_w(par, tok, cum, root, rows[:n], n, w)
+    par2 = np.r_[par, p].astype(np.int32)
+    tok2 = np.r_[tok, t].astype(np.int32)
+    cum2 = oracle.cumulative_scores(par2, tok2, root, rows, n + w)
+    np.testing.assert_allclose(cum2[:n], cum, rtol=0, atol=0)
+    np.testing.assert_allclose(cum2[n:], s, rtol=1e-13, atol=1e-13)
