@@ -97,3 +97,79 @@ def assert_attn_close(O, L, O_ref, L_ref, dtype, rows_mask=None, what=""):
                     f"{np.isnan(o).any() or np.isnan(l).any()}")
             worst = max(worst, float((eo / bound_o).max()), float((el / bound_l).max()))
     return worst
+
+
+# ----------------------------------------------------------------------------
+# Closed form of attention on the counting inputs (gen.structured): with zero
+# queries every visible score is 0, so a row's LSE is ln(number of visible
+# positions) = ln(P + depth(node)) and its output is the mean of the visible
+# value rows (SwiftSpec summary, Section 3.1.3 Figure 3: prefix + ancestors +
+# self; the zero-query closed form pinned in tests/test_oracle_attention.py).
+# ----------------------------------------------------------------------------
+
+def counting_expected(case, n_q, q_nodes_of):
+    """Exact (float64) O [B][n_q][Hq][d] and LSE [B][Hq][n_q] of ``case`` built
+    by ``gen.structured.counting_inputs`` (or a batch slice of one, with its
+    ``planted["id_codes"]`` sliced alike); ``q_nodes_of(n)`` lists the node of
+    each of the n_q query rows (verify: range(n_max); expand: n - w + r).
+    Rows without a node are NaN."""
+    import oracle
+    from gen.structured import TILE, TREE_CODES, n_prefix_channels
+    B, Hq, d = case.B, case.Hq, case.d
+    G, Hkv = case.G, case.Hkv
+    npc = n_prefix_channels(d)
+    O = np.full((B, n_q, Hq, d), np.nan)
+    L = np.full((B, Hq, n_q), np.nan)
+    ids = np.repeat(np.asarray(case.planted["id_codes"], float), G, axis=1)   # [B][Hq]
+    for b in range(B):
+        P, n = int(case.prefix_len[b]), int(case.n_nodes[b])
+        pref = np.bincount((np.arange(P) // TILE) % npc, minlength=npc).astype(float)
+        for r, i in enumerate(q_nodes_of(n)):
+            if not 0 <= i < n:
+                continue
+            vis = [int(x) for x in oracle.tree.visible_tree_columns(case.parent[b], i)]
+            cnt = P + len(vis)
+            tree = np.bincount(np.array(vis) % TREE_CODES, minlength=TREE_CODES).astype(float)
+            row = np.r_[pref, tree, 0.0] / cnt
+            O[b, r] = row[None, :]
+            O[b, r, :, d - 1] = ids[b]
+            L[b, :, r] = np.log(cnt)
+    return O, L
+
+
+def assert_counting_exact(O, L, O_x, L_x, what=""):
+    """Bars for the counting inputs, from the arithmetic the kernels do on
+    them: every probability is exactly 1 and every value an integer, so the
+    fp32 sums are exact integers; LSE = (0 + log2 l) * ln 2 is within a few
+    float32 ulp of ln l (hardware log2 ~1 ulp, the product 0.5 ulp); the
+    output is count * (1/l) (two fp32 roundings) rounded once to bf16
+    (half a bf16 ulp, at most 2^-8 relative).  Zero channels must be exactly
+    zero and the identity channel exactly its integer code."""
+    rows = ~np.isnan(O_x[..., 0, 0])
+    Lr = np.transpose(L, (0, 2, 1))[rows]            # [rows][Hq]
+    Lx = np.transpose(L_x, (0, 2, 1))[rows]
+    ulp = np.spacing(np.abs(Lx).astype(np.float32)).astype(np.float64)
+    errL = np.abs(Lr - Lx) / ulp
+    if not np.all(errL <= 4.0):
+        i = np.unravel_index(np.argmax(errL), errL.shape)
+        raise AssertionError(f"{what}: LSE off by {errL[i]:.1f} fp32 ulp at row {i} "
+                             f"(got {Lr[i]!r}, expected {Lx[i]!r})")
+    Og, Ox = O[rows], O_x[rows]
+    bound = (2.0 ** -8 + 2.0 ** -20) * np.abs(Ox)
+    bad = np.abs(Og - Ox) > bound
+    if bad.any():
+        i = np.unravel_index(np.argmax(np.abs(Og - Ox) - bound), Og.shape)
+        raise AssertionError(f"{what}: output channel off at (row, head, channel) {i}: "
+                             f"got {Og[i]!r}, expected {Ox[i]!r}; {int(bad.sum())} bad values")
+    return float(errL.max())
+
+
+def assert_lse_tight(L, L_ref, bound, what=""):
+    """|LSE - LSE_ref| <= bound on every output row (NaN rows of the
+    reference are skipped)."""
+    ok = ~np.isnan(L_ref)
+    err = np.abs(L[ok] - L_ref[ok])
+    if not np.all(err <= bound):
+        raise AssertionError(f"{what}: max |dLSE| = {np.nanmax(err):.3e} > {bound:.1e} "
+                             f"({int((err > bound).sum())} rows)")
+    return float(err.max()) if err.size else 0.0

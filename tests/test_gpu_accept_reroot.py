@@ -171,3 +171,92 @@ def test_reroot_fig4_on_gpu(ta, golden):
     kk = kv.k.cpu().numpy()
     for row, old in fx["expected_rows_old_position"].items():
         np.testing.assert_array_equal(kk[0, int(row)], k[0, old])
+
+
+def _duplicate_sibling_case(seed, B, n_max, vocab):
+    """Trees whose siblings often share a token (tokens drawn from a tiny
+    vocabulary) and integer-valued logits (frequent argmax ties), so that
+    several accepted nodes reach the maximum depth: the deepest-then-lowest-
+    index rule (draft-length co-design article, Acceptance Length: the
+    longest accepted path) decides between them."""
+    rng = np.random.default_rng([seed, 31])
+    parent = np.full((B, n_max), -1, dtype=np.int32)
+    n_nodes = rng.integers(1, n_max + 1, size=B).astype(np.int32)
+    for b in range(B):
+        for i in range(1, int(n_nodes[b])):
+            parent[b, i] = rng.integers(-1, i) if seed % 2 else rng.integers(max(-1, i - 3), i)
+    tok = rng.integers(0, vocab, size=(B, n_max)).astype(np.int32)
+    logits = rng.integers(-2, 3, size=(B, n_max, vocab)).astype(np.float32)
+    root_tok = np.array([tok[b, 0] for b in range(B)], dtype=np.int32)
+    return parent, tok, logits, root_tok, n_nodes
+
+
+def _tied_deepest(parent, tok, logits, root_tok, n):
+    """Number of accepted nodes at the maximum accepted depth (brute force)."""
+    a = [oracle.argmax_first(logits[i]) for i in range(n)]
+    depths = []
+    for i in range(n):
+        rp = oracle.root_path(parent, i)
+        ok = tok[rp[0]] == root_tok and all(tok[y] == a[x] for x, y in zip(rp[:-1], rp[1:]))
+        if ok:
+            depths.append(len(rp))
+    return depths.count(max(depths)) if depths else 0
+
+
+@pytest.mark.parametrize("seed,n_max,vocab,ldt", [
+    (1, 12, 2, "f32"), (2, 24, 2, "f32"), (3, 64, 2, "bf16"), (4, 256, 2, "f32"),
+    (5, 40, 3, "bf16")])
+def test_accept_duplicate_sibling_ties(ta, seed, n_max, vocab, ldt):
+    import torch
+    B = 48
+    parent, tok, logits, root_tok, n_nodes = _duplicate_sibling_case(seed, B, n_max, vocab)
+    ties = sum(_tied_deepest(parent[b], tok[b], logits[b], root_tok[b], int(n_nodes[b])) >= 2
+               for b in range(B))
+    assert ties >= B // 8, "the case must exercise ties between deepest accepted nodes"
+    lg = torch.from_numpy(logits)
+    if ldt == "bf16":
+        lg = lg.to(torch.bfloat16)      # small integers: exact in bf16
+    path, plen, bonus = ta.accept_greedy_path(lg.cuda(), dev_tensor(parent), dev_tensor(tok),
+                                              dev_tensor(n_nodes), dev_tensor(root_tok))
+    torch.cuda.synchronize()
+    pr, lr, br = oracle.accept_greedy_path(logits, parent, tok, n_nodes, root_tok)
+    np.testing.assert_array_equal(plen.cpu().numpy(), lr)
+    np.testing.assert_array_equal(path.cpu().numpy(), pr)
+    np.testing.assert_array_equal(bonus.cpu().numpy(), br)
+
+
+@pytest.mark.parametrize("seed,keep", [(11, True), (12, False), (13, None)])
+def test_accept_then_reroot_with_duplicate_siblings(ta, seed, keep):
+    """The GPU's accepted path feeds the GPU re-root on duplicate-sibling
+    trees; paths, metadata and every kept KV byte against the oracle."""
+    import torch
+    B, n_max, Hkv, d = 24, 48, 2, 128
+    parent, tok, logits, root_tok, n_nodes = _duplicate_sibling_case(seed, B, n_max, 2)
+    rng = np.random.default_rng(seed)
+    P = rng.integers(0, 40, size=B).astype(np.int32)
+    T_cap = int(P.max()) + n_max
+    k = rng.standard_normal((B, T_cap, Hkv, d), dtype=np.float32)
+    v = rng.standard_normal((B, T_cap, Hkv, d), dtype=np.float32)
+    keep_np = np.array([keep if keep is not None else bool(rng.integers(0, 2))
+                        for _ in range(B)], dtype=np.uint8)
+    d_par, d_P, d_n = dev_tensor(parent), dev_tensor(P), dev_tensor(n_nodes)
+    kv = ta.KVCache(dev_tensor(k), dev_tensor(v))
+    path, plen, bonus = ta.accept_greedy_path(dev_tensor(logits), d_par, dev_tensor(tok), d_n,
+                                              dev_tensor(root_tok))
+    ta.tree_cache_reroot([kv], d_P, d_par, d_n, path, plen, dev_tensor(keep_np))
+    torch.cuda.synchronize()
+    pr, lr, br = oracle.accept_greedy_path(logits, parent, tok, n_nodes, root_tok)
+    np.testing.assert_array_equal(path.cpu().numpy(), pr)
+    np.testing.assert_array_equal(plen.cpu().numpy(), lr)
+    np.testing.assert_array_equal(bonus.cpu().numpy(), br)
+    layers, P1, par1, n1 = oracle.tree_cache_reroot([(k, v)], P, parent, n_nodes, pr, lr,
+                                                    keep_np.astype(bool))
+    np.testing.assert_array_equal(d_P.cpu().numpy(), P1)
+    np.testing.assert_array_equal(d_n.cpu().numpy(), n1)
+    np.testing.assert_array_equal(d_par.cpu().numpy(), par1)
+    kg, vg = _kv_bits(kv.k), _kv_bits(kv.v)
+    kr, vr = layers[0][0].view(np.int32), layers[0][1].view(np.int32)
+    for b in range(B):
+        e = int(P1[b] + n1[b])
+        np.testing.assert_array_equal(kg[b, :e], kr[b, :e])
+        np.testing.assert_array_equal(vg[b, :e], vr[b, :e])

@@ -1,0 +1,237 @@
+"""Full-size attention parity that can fail.
+
+At the chain-verify size (16 sequences x 32768 prefix positions) one 32-position
+KV tile holds about 1/1000 of the softmax mass of N(0, 1) data, so the stated
+bf16 bars (2e-2 absolute + 1e-2 relative) would let a dropped, repeated or
+misplaced tile through.  These tests run the hot-path kernels at the full
+chain-verify and paged-alternating sizes, in the configuration the benchmark
+uses and through each kernel that serves those layouts, on inputs where every
+tile is visible in the outputs (gen.structured):
+
+* counting inputs (zero queries): the exact closed form of the zero-query
+  case -- LSE = ln(P + depth), output = mean of the visible value rows, whose
+  indicator codes name each tile and node -- within a few fp32 ulp;
+* needle inputs: one strong key per tile, its value coded by tile, against
+  the float64 oracle with bars derived from the kernels' arithmetic;
+* the N(0, 1) chain-verify workload: all 128 (sequence, KV head) blocks
+  against the oracle, with the stated bars plus a derived LSE bar.
+
+Detection margins (chain verify, P = 32768): a missing 32-position tile moves
+the counting LSE by ln(32784 / 32752) = 9.8e-4, about a thousand fp32 ulp,
+and its code channel by 1/9 of its value; in the needle inputs a tile read
+with another tile's keys drops its code channel by at least 3 % against a
+0.8 % bar; for N(0, 1) data a tile carries 0.75e-3 .. 1.2e-3 of the mass
+against the 1e-4 LSE bar.
+"""
+import gc
+
+import numpy as np
+import pytest
+
+from helpers import (DevCase, assert_attn_close, assert_counting_exact, assert_lse_tight,
+                     counting_expected, ensure_built, to_f64)
+
+import oracle
+from gen import config2_chain, config5_paged
+from gen.structured import counting_inputs, needle_inputs
+
+pytestmark = pytest.mark.gpu
+
+# Derived bound on |LSE - LSE_oracle| for bf16 inputs at these sizes: the
+# scores are fp32 dot products of exact bf16 products (error < 2e-6 in the
+# exponent), each exponential is within ~1 ulp, and a row's sum runs through
+# fewer than ~300 sequential fp32 additions per split (16 per tile, one per
+# tile, a few split merges), i.e. a relative error below 300 * 2^-24 = 1.8e-5;
+# the log adds a few ulp.  1e-4 is five times that worst case.
+LSE_TIGHT = 1e-4
+
+# Needle inputs: the value channels hold sums of needle probabilities, each
+# rounded to bf16 (8 significant bits: relative error up to 2^-8) before the
+# P.V product, all terms of one sign; then the output is rounded once more to
+# bf16 (2^-8); fp32 sums and the division add ~2^-20.  Measured on the MFMA
+# kernels: 0.70 % at most, against 0.39 % for the fp32 VALU kernel, whose
+# probabilities are not rounded.
+NEEDLE_RTOL = 2.0 ** -8 + 2.0 ** -8 + 2.0 ** -16
+
+
+@pytest.fixture(scope="module")
+def ta():
+    ensure_built()
+    import tree_masked_verify_attn_amd as m
+    return m
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+def _release():
+    """Return the device memory of the caller's dropped tensors."""
+    import torch
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def _verify_batch(ta, dc, kernel, sl=None):
+    """tree_attn_verify over sequences ``sl`` (all by default) with the
+    automatic kernel (0) or a forced one; returns float64 (O, LSE)."""
+    if sl is None:
+        sl = slice(0, dc.case.B)
+    kv = dc.kv
+    if dc.block_table is not None:
+        kv = type(dc.kv)(dc.k, dc.v, dc.block_table[sl].contiguous(), T_cap=dc.case.T_cap)
+    out, lse = ta.tree_attn_verify(dc.q[sl].contiguous(), kv, dc.prefix_len[sl].contiguous(),
+                                   dc.parent[sl].contiguous(), dc.n_nodes[sl].contiguous(),
+                                   dc.case.scale, kernel=kernel)
+    _sync()
+    return to_f64(out), lse.cpu().numpy().astype(np.float64)
+
+
+def _sub(c, sl):
+    import copy
+    s = copy.copy(c)
+    s.q = c.q[sl]
+    s.prefix_len = c.prefix_len[sl]
+    s.parent = c.parent[sl]
+    s.n_nodes = c.n_nodes[sl]
+    if c.block_table is not None:
+        s.block_table = c.block_table[sl]
+    if "id_codes" in c.planted:
+        s.planted = dict(c.planted, id_codes=c.planted["id_codes"][sl])
+    s.B = s.q.shape[0]
+    return s
+
+
+def _batches(c):
+    m = c.planted.get("batch_size")
+    if m is None:
+        return [slice(0, c.B)]
+    return [slice(s * m, (s + 1) * m) for s in range(c.B // m)]
+
+
+# ----------------------------------------------------------------------------
+# counting inputs: exact closed form
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kernel", [0, 2])
+def test_counting_chain_verify(ta, kernel):
+    c = counting_inputs(config2_chain())
+    dc = DevCase(c)
+    O, L = _verify_batch(ta, dc, kernel)
+    Ox, Lx = counting_expected(c, c.n_max, lambda n: list(range(c.n_max)))
+    assert_counting_exact(O, L, Ox, Lx, what=f"chain verify, kernel {kernel}")
+    if kernel == 0:
+        # expand rows at full size: the 4 newest nodes
+        import torch
+        w = 4
+        out, lse = ta.tree_attn_expand(dc.q[:, :w].contiguous(), dc.kv, dc.prefix_len,
+                                       dc.parent, dc.n_nodes, c.scale)
+        _sync()
+        Oxe, Lxe = counting_expected(c, w, lambda n: [n - w + r for r in range(w)])
+        assert_counting_exact(to_f64(out), lse.cpu().numpy().astype(np.float64), Oxe, Lxe,
+                              what="chain expand")
+        del out, lse, torch
+    del dc
+    _release()
+
+
+@pytest.mark.parametrize("kernel", [0, 2, 3])
+def test_counting_paged_alternating(ta, kernel):
+    c = counting_inputs(config5_paged())
+    dc = DevCase(c)
+    for s, sl in enumerate(_batches(c)):
+        O, L = _verify_batch(ta, dc, kernel, sl)
+        sub = _sub(c, sl)
+        Ox, Lx = counting_expected(sub, sub.n_max, lambda n: list(range(sub.n_max)))
+        assert_counting_exact(O, L, Ox, Lx, what=f"paged batch {s}, kernel {kernel}")
+    del dc
+    _release()
+
+
+# ----------------------------------------------------------------------------
+# needle inputs: float64 oracle, derived bars
+# ----------------------------------------------------------------------------
+
+def _assert_needles(O, L, Or, Lr, what):
+    rows = ~np.isnan(Or[..., 0, 0])
+    Og, Ox = O[rows], Or[rows]
+    # identity channel: a constant's weighted mean, the integer code exactly on
+    # the GPU (integer partial sums, one rounding to bf16); the fp64 oracle
+    # reaches it up to its own rounding
+    code = np.rint(Ox[..., -1])
+    assert np.all(np.abs(Ox[..., -1] - code) < 1e-9)
+    np.testing.assert_array_equal(Og[..., -1], code, err_msg=f"{what}: identity codes")
+    bound = NEEDLE_RTOL * np.abs(Ox[..., :-1]) + 1e-30
+    err = np.abs(Og[..., :-1] - Ox[..., :-1])
+    if not np.all(err <= bound):
+        i = np.unravel_index(np.argmax(err - bound), err.shape)
+        raise AssertionError(f"{what}: code channel off at (row, head, channel) {i}: got "
+                             f"{Og[..., :-1][i]!r}, oracle {Ox[..., :-1][i]!r}")
+    assert_lse_tight(L, Lr, LSE_TIGHT, what)
+
+
+@pytest.fixture(scope="module")
+def chain_needles():
+    c = needle_inputs(config2_chain(), seed=2)
+    Or, Lr = oracle.verify(c)
+    yield c, Or, Lr
+    del c, Or, Lr
+    gc.collect()
+
+
+@pytest.mark.parametrize("kernel", [0, 2])
+def test_needles_chain_verify(ta, chain_needles, kernel):
+    c, Or, Lr = chain_needles
+    dc = DevCase(c)
+    O, L = _verify_batch(ta, dc, kernel)
+    _assert_needles(O, L, Or, Lr, f"chain verify needles, kernel {kernel}")
+    del dc
+    _release()
+
+
+@pytest.fixture(scope="module")
+def paged_needles():
+    c = needle_inputs(config5_paged(), seed=5)
+    refs = [oracle.verify(_sub(c, sl)) for sl in _batches(c)]
+    yield c, refs
+    del c, refs
+    gc.collect()
+
+
+@pytest.mark.parametrize("kernel", [0, 2, 3])
+def test_needles_paged_alternating(ta, paged_needles, kernel):
+    c, refs = paged_needles
+    dc = DevCase(c)
+    for s, sl in enumerate(_batches(c)):
+        O, L = _verify_batch(ta, dc, kernel, sl)
+        _assert_needles(O, L, refs[s][0], refs[s][1], f"paged needles batch {s}, kernel {kernel}")
+    del dc
+    _release()
+
+
+# ----------------------------------------------------------------------------
+# the N(0, 1) workloads: every block against the oracle
+# ----------------------------------------------------------------------------
+
+def test_chain_verify_all_blocks(ta):
+    c = config2_chain()
+    dc = DevCase(c)
+    O, L = _verify_batch(ta, dc, 0)
+    del dc
+    _release()
+    Or, Lr = oracle.verify(c)
+    assert_attn_close(O, L, Or, Lr, "bf16", what="chain verify")
+    assert_lse_tight(L, Lr, LSE_TIGHT, "chain verify")
+
+
+def test_paged_alternating_all_blocks_tight_lse(ta):
+    c = config5_paged()
+    dc = DevCase(c)
+    for s, sl in enumerate(_batches(c)):
+        O, L = _verify_batch(ta, dc, 0, sl)
+        Or, Lr = oracle.verify(_sub(c, sl))
+        assert_attn_close(O, L, Or, Lr, "bf16", what=f"paged batch {s}")
+        assert_lse_tight(L, Lr, LSE_TIGHT, f"paged batch {s}")
+    del dc
+    _release()

@@ -1,7 +1,7 @@
 """The five seeded workloads at full size, in the launch configuration the
-benchmark uses (automatic kernel and split choice), against the oracle:
-every output where the oracle is cheap, sampled (sequence, KV head) blocks
-for the 2.1 GB chain-verify case."""
+benchmark uses (automatic kernel and split choice), against the oracle.
+The chain-verify attention (2.1 GB of KV) is compared in
+test_gpu_fullsize.py, every block, with structured inputs beside it."""
 import numpy as np
 import pytest
 
@@ -154,22 +154,12 @@ def test_config4_draft_expansion_rounds(ta):
         rows = np.r_[rows, c.logits_new[r]]
 
 
-def test_config2_chain_verify_sampled(ta):
+def test_config2_chain_accept_reroot(ta):
+    """Accept and re-root on the chain-verify workload (its attention is
+    compared block by block in test_gpu_fullsize.py)."""
     import torch
     c = config2_chain()
     dc = DevCase(c)
-    O, L = _verify(ta, dc)
-    rng = np.random.default_rng(22)
-    for b in rng.choice(c.B, size=3, replace=False):
-        hk = int(rng.integers(0, c.Hkv))
-        heads = list(range(hk * c.G, (hk + 1) * c.G))
-        Or, Lr = oracle.verify(c, batches=[int(b)], heads=heads)
-        sl = slice(int(b), int(b) + 1)
-        assert_attn_close(O[sl][:, :, heads], L[sl][:, heads], Or[sl][:, :, heads],
-                          Lr[sl][:, heads], "bf16", what=f"config2 b={b} hkv={hk}")
-    # property that holds at any size: every output is finite, every LSE is at
-    # least the log of the visible count's lower bound (all scores finite)
-    assert np.isfinite(O).all() and np.isfinite(L).all()
     pr, lr = _accept_and_reroot(ta, dc, keep=False)
     assert lr.tolist() == c.planted["path_len"]
     del dc

@@ -138,7 +138,8 @@ def test_duplicate_siblings_take_deepest_then_lowest_index():
     logits[0, 0, 1] = 1.0
     po, pl, bo = oracle.accept_greedy_path(logits, parent, tok, np.array([4]), np.array([4]))
     assert pl[0] == 2 and po[0, :2].tolist() == [1, 2]
-    # both branches reach depth 2 -> the lower node index (3 under node 0) wins
+    # both branches reach depth 2 (node 2 under node 1, node 3 under node 0):
+    # the lower node index, node 2, wins
     logits[0, 0, 6] = 2.0
     po, pl, bo = oracle.accept_greedy_path(logits, parent, tok, np.array([4]), np.array([4]))
     assert pl[0] == 2 and po[0, :2].tolist() == [1, 2]
