@@ -64,7 +64,9 @@ typedef enum {
   TA_ERR_UNSUPPORTED = -2,     /* d not in {64,128}, unknown dtype, ...          */
   TA_ERR_TREE_TOO_LARGE = -3,  /* n_max > TA_MAX_NODES                           */
   TA_ERR_WORKSPACE = -4,       /* workspace missing or smaller than required     */
-  TA_ERR_HIP = -5              /* a HIP runtime call or kernel launch failed     */
+  TA_ERR_HIP = -5,             /* a HIP runtime call or kernel launch failed     */
+  TA_ERR_SCRATCH = -6          /* tree_attn_verify_noalloc: the call's plan needs
+                                  more than TA_NOALLOC_SCRATCH_BYTES            */
 } ta_status;
 
 typedef enum { TA_F32 = 0, TA_BF16 = 1 } ta_dtype;
@@ -329,6 +331,27 @@ int tree_token_walk(const int32_t* parent, const int32_t* tok, const int32_t* n_
 int tree_select_subtree(const float* cum, const int32_t* parent, const int32_t* tok,
                         const int32_t* n_nodes, int B, int n_max, int bs, int32_t* sel_node,
                         int32_t* sel_parent, int32_t* sel_tok, int32_t* sel_n, void* stream);
+
+/*
+ * tree_attn_verify for callers that cannot allocate memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, kernels, plan and results as tree_attn_verify, without the
+ * workspace pair: the split-KV partial results go to a fixed device array of
+ * TA_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends (its address is looked up once per device, on the
+ * first call there).  The call allocates nothing.  A call whose plan needs
+ * more than that (tree_attn_workspace_bytes tells) returns TA_ERR_SCRATCH
+ * before any launch; the automatic plans of calls with d <= 128 on a
+ * 256-compute-unit MI355X need at most 68.2 MB.  Every call on one GPU shares
+ * that GPU's array and it keeps the last call's contents (the kernels
+ * initialise what they read), so calls that overlap in time on one GPU race:
+ * order them on one stream.  `stream` must belong to the current device.
+ */
+#define TA_NOALLOC_SCRATCH_BYTES ((size_t)72 << 20)
+int tree_attn_verify_noalloc(const void* q, ta_kv kv, const int32_t* prefix_len,
+                             const int32_t* parent, const int32_t* n_nodes, int B, int n_max,
+                             int Hq, int Hkv, int d, int dtype, float scale, void* out,
+                             float* lse, const ta_attn_opts* opts, void* stream);
 
 /* Human-readable name of a ta_status value (static string). */
 const char* ta_status_string(int status);

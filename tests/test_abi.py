@@ -26,7 +26,7 @@ def test_library_exports_every_symbol():
     for name in _lib.EXPORTED_SYMBOLS:
         assert re.search(rf"\bT {name}$", out, re.M), name
     assert ta.ta_version() == "0.1.0"
-    for st in (0, -1, -2, -3, -4, -5):
+    for st in (0, -1, -2, -3, -4, -5, -6):
         assert ta.ta_status_string(st).startswith("TA_")
 
 

@@ -6,6 +6,7 @@ entry points keep the C names:
 
 * ``tree_attn_verify``   -- tree-masked attention over every draft node
 * ``tree_attn_expand``   -- the same for the w newest leaves (non-square mask)
+* ``tree_attn_verify_noalloc`` -- verify with the library's fixed scratch (no allocation)
 * ``accept_greedy_path`` -- greedy longest accepted path, AL and bonus token
 * ``accept_sampling_path`` -- the same by speculative sampling (temperature > 0)
 * ``tree_cache_reroot``  -- evolving-tree-cache re-root with in-place KV moves
@@ -31,6 +32,7 @@ from ._lib import (  # noqa: F401
     ta_version,
     tree_attn_expand,
     tree_attn_verify,
+    tree_attn_verify_noalloc,
     tree_attn_workspace_bytes,
     tree_cache_reroot,
     tree_expand_top_w,

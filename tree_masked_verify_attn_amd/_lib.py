@@ -21,6 +21,7 @@ TA_ERR_UNSUPPORTED = -2
 TA_ERR_TREE_TOO_LARGE = -3
 TA_ERR_WORKSPACE = -4
 TA_ERR_HIP = -5
+TA_ERR_SCRATCH = -6
 TA_F32 = 0
 TA_BF16 = 1
 TA_MAX_NODES = 256
@@ -30,6 +31,7 @@ EXPORTED_SYMBOLS = (
     "tree_attn_workspace_bytes",
     "tree_attn_verify",
     "tree_attn_expand",
+    "tree_attn_verify_noalloc",
     "accept_greedy_path",
     "accept_sampling_path",
     "accept_sampling_workspace_bytes",
@@ -97,6 +99,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.tree_attn_expand.argtypes = attn + [c_int] * 7 + [f32, vp, vp, vp, c_size,
                                                               ctypes.POINTER(ta_attn_opts), vp]
         lib.tree_attn_expand.restype = c_int
+        lib.tree_attn_verify_noalloc.argtypes = attn + [c_int] * 6 + [
+            f32, vp, vp, ctypes.POINTER(ta_attn_opts), vp]
+        lib.tree_attn_verify_noalloc.restype = c_int
         lib.accept_greedy_path.argtypes = [vp, c_int, vp, vp, vp, vp, c_int, c_int, c_int, vp, vp,
                                            vp, vp]
         lib.accept_greedy_path.restype = c_int
@@ -287,6 +292,8 @@ def _workspace_for(device, nbytes):
 
 def _attention(fn_name, q, kv: KVCache, prefix_len, parent, n_nodes, scale, out, lse, workspace,
                w, chunk_tokens, kernel, stream, with_lse):
+    """Marshals one attention call; ``fn_name`` is "verify", "expand" or
+    "verify_noalloc" (no workspace: the library's fixed scratch array)."""
     torch = _torch()
     lib = load_library()
     _need(q, "q", dtype=kv.dtype, ndim=4, device=kv.k.device)
@@ -317,6 +324,16 @@ def _attention(fn_name, q, kv: KVCache, prefix_len, parent, n_nodes, scale, out,
         _need(lse, "lse", dtype=torch.float32, device=dev)
         if tuple(lse.shape) != (B, Hq, n_q):
             raise ValueError("lse must be [B][Hq][n_q]")
+    common = (q.data_ptr(), kv.struct(), prefix_len.data_ptr(), parent.data_ptr(),
+              n_nodes.data_ptr())
+    if fn_name == "verify_noalloc":
+        if n_q != n_max:
+            raise ValueError("verify queries must be [B][n_max][Hq][d]")
+        st = lib.tree_attn_verify_noalloc(*common, B, n_max, Hq, kv.Hkv, d, dt,
+                                          ctypes.c_float(scale), out.data_ptr(), _ptr(lse),
+                                          _opts(chunk_tokens, kernel), _stream(stream))
+        _check(st)
+        return out, lse
     nbytes = tree_attn_workspace_bytes(B, n_q, Hq, kv.Hkv, d, dt, kv.T_cap, chunk_tokens, kernel)
     if workspace is None:
         ws = _workspace_for(dev, nbytes)
@@ -325,8 +342,6 @@ def _attention(fn_name, q, kv: KVCache, prefix_len, parent, n_nodes, scale, out,
     if ws is not None:
         _need(ws, "workspace", device=dev)   # device memory of this call's GPU only
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
-    common = (q.data_ptr(), kv.struct(), prefix_len.data_ptr(), parent.data_ptr(),
-              n_nodes.data_ptr())
     tail = (ctypes.c_float(scale), out.data_ptr(), _ptr(lse), _ptr(ws), ws_bytes,
             _opts(chunk_tokens, kernel), _stream(stream))
     if fn_name == "verify":
@@ -345,6 +360,17 @@ def tree_attn_verify(q, kv: KVCache, prefix_len, parent, n_nodes, scale: float, 
     """Verification attention over every tree node; returns ``(out, lse)``."""
     return _attention("verify", q, kv, prefix_len, parent, n_nodes, scale, out, lse, workspace,
                       0, chunk_tokens, kernel, stream, with_lse)
+
+
+def tree_attn_verify_noalloc(q, kv: KVCache, prefix_len, parent, n_nodes, scale: float, out=None,
+                             lse=None, chunk_tokens: int = 0, kernel: int = 0, stream=None,
+                             with_lse: bool = True):
+    """tree_attn_verify without a workspace: the library keeps the split
+    partial results in its fixed per-GPU scratch array and allocates nothing
+    (pass ``out`` and ``lse`` to allocate nothing on this side either).
+    Calls that overlap in time on one GPU race on that array."""
+    return _attention("verify_noalloc", q, kv, prefix_len, parent, n_nodes, scale, out, lse,
+                      None, 0, chunk_tokens, kernel, stream, with_lse)
 
 
 def tree_attn_expand(q, kv: KVCache, prefix_len, parent, n_nodes, scale: float, out=None,

@@ -151,10 +151,15 @@ int check_kv(const ta_kv& kv) {
   return TA_OK;
 }
 
+}  // namespace
+
+namespace ta {
+
 int run_attention(const void* q, ta_kv kv, const int32_t* prefix_len, const int32_t* parent,
                   const int32_t* n_nodes, int B, int n_q, int n_max, int expand, int Hq, int Hkv,
                   int d, int dtype, float scale, void* out, float* lse, void* ws,
-                  size_t ws_bytes, const ta_attn_opts* opts, void* stream) {
+                  size_t ws_bytes, const ta_attn_opts* opts, void* stream,
+                  ScratchFn scratch) {
   int st = check_common(B, n_q, n_max, Hq, Hkv, d, dtype, kv.T_cap);
   if (st != TA_OK) return st;
   st = check_kv(kv);
@@ -174,6 +179,12 @@ int run_attention(const void* q, ta_kv kv, const int32_t* prefix_len, const int3
   if (pl.kernel == 3 && kv.block_table != nullptr &&
       pl.chunk / kv.block_size + 2 > ta::kStreamMaxSplitBlocks)
     pl.kernel = 2;
+  if (scratch != nullptr && pl.ws_bytes > 0) {
+    // the library's own scratch array stands in for the caller's workspace
+    st = scratch(pl.ws_bytes, stream, &ws);
+    if (st != TA_OK) return st;
+    ws_bytes = pl.ws_bytes;
+  }
   if (pl.ws_bytes > 0 && (ws == nullptr || ws_bytes < pl.ws_bytes || !aligned16(ws)))
     return TA_ERR_WORKSPACE;
 
@@ -246,7 +257,7 @@ int run_attention(const void* q, ta_kv kv, const int32_t* prefix_len, const int3
   return hip_status(e, where);
 }
 
-}  // namespace
+}  // namespace ta
 
 extern "C" {
 
@@ -267,8 +278,8 @@ int tree_attn_verify(const void* q, ta_kv kv, const int32_t* prefix_len, const i
                      const int32_t* n_nodes, int B, int n_max, int Hq, int Hkv, int d, int dtype,
                      float scale, void* out, float* lse, void* ws, size_t ws_bytes,
                      const ta_attn_opts* opts, void* stream) {
-  return run_attention(q, kv, prefix_len, parent, n_nodes, B, n_max, n_max, 0, Hq, Hkv, d, dtype,
-                       scale, out, lse, ws, ws_bytes, opts, stream);
+  return ta::run_attention(q, kv, prefix_len, parent, n_nodes, B, n_max, n_max, 0, Hq, Hkv, d,
+                           dtype, scale, out, lse, ws, ws_bytes, opts, stream, nullptr);
 }
 
 int tree_attn_expand(const void* q, ta_kv kv, const int32_t* prefix_len, const int32_t* parent,
@@ -276,8 +287,8 @@ int tree_attn_expand(const void* q, ta_kv kv, const int32_t* prefix_len, const i
                      int dtype, float scale, void* out, float* lse, void* ws, size_t ws_bytes,
                      const ta_attn_opts* opts, void* stream) {
   if (w < 1 || w > n_max) return TA_ERR_INVALID_ARG;
-  return run_attention(q, kv, prefix_len, parent, n_nodes, B, w, n_max, 1, Hq, Hkv, d, dtype,
-                       scale, out, lse, ws, ws_bytes, opts, stream);
+  return ta::run_attention(q, kv, prefix_len, parent, n_nodes, B, w, n_max, 1, Hq, Hkv, d, dtype,
+                           scale, out, lse, ws, ws_bytes, opts, stream, nullptr);
 }
 
 int accept_greedy_path(const void* logits, int logit_dtype, const int32_t* parent,
@@ -468,6 +479,9 @@ const char* ta_status_string(int status) {
     case TA_ERR_TREE_TOO_LARGE: return "TA_ERR_TREE_TOO_LARGE: more than 256 tree nodes";
     case TA_ERR_WORKSPACE: return "TA_ERR_WORKSPACE: workspace missing or too small";
     case TA_ERR_HIP: return "TA_ERR_HIP: HIP launch or runtime failure";
+    case TA_ERR_SCRATCH:
+      return "TA_ERR_SCRATCH: the call needs more than the 72 MiB scratch array of "
+             "tree_attn_verify_noalloc";
     default: return "unknown ta_status";
   }
 }

@@ -66,6 +66,16 @@ struct AttnParams {
   int32_t* ws_seq;
 };
 
+// One attention call (tree_attn_verify / tree_attn_expand): validation,
+// planning, launches.  With `scratch` set, the workspace arguments are
+// ignored and scratch(bytes the plan needs, stream, &ws) supplies the buffer
+// once the plan is known (only when the plan needs one).
+typedef int (*ScratchFn)(size_t need, void* stream, void** ws);
+int run_attention(const void* q, ta_kv kv, const int32_t* prefix_len, const int32_t* parent,
+                  const int32_t* n_nodes, int B, int n_q, int n_max, int expand, int Hq, int Hkv,
+                  int d, int dtype, float scale, void* out, float* lse, void* ws,
+                  size_t ws_bytes, const ta_attn_opts* opts, void* stream, ScratchFn scratch);
+
 // Workspace layout: the partial outputs, then the (max, sum) pairs.  Returns
 // the bytes needed for a plan (0 when there is a single split).
 size_t attn_ws_bytes(int tiles, int n_split, int rows_per_tile, int d);
