@@ -47,7 +47,7 @@ from .bf16 import bf16_to_f64, to_f64  # noqa: F401
 from .tree import ancestors, depth, descendants, is_valid_parent, root_path  # noqa: F401
 from .attention import tree_attention, verify, expand, gather_sequence_kv  # noqa: F401
 from .accept import accept_greedy_path, argmax_first  # noqa: F401
-from .reroot import tree_cache_reroot  # noqa: F401
+from .reroot import reroot_node_arrays, tree_cache_reroot  # noqa: F401
 from .topw import cumulative_scores, select_top_w  # noqa: F401
 from .draft import token_walk, select_subtree  # noqa: F401
 from .rope import rope, tree_positions, rope_append  # noqa: F401

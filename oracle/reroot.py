@@ -69,3 +69,38 @@ def tree_cache_reroot(kv_layers, prefix_len, parent, n_nodes, path, path_len, ke
         P_out[b] = P + k
         n_out[b] = len(kept)
     return new_layers, P_out, par_out, n_out
+
+
+def reroot_node_arrays(parent, n: int, path, k: int, keep: bool, tok, cum=None):
+    """The per-node arrays the draft keeps beside its tree, after the re-root
+    of one sequence (SwiftSpec summary, Section 3.1.1 Algorithm 1: Re-root,
+    then Select on the re-rooted tree; Section 3.2: the kept subtree is pulled
+    forward).
+
+    ``tok`` (node tokens) and ``cum`` (cumulative log-probabilities, the
+    weights of the maximum-likelihood expansion, Section 3.1.3) follow the
+    node mapping of ``tree_cache_reroot``: kept node ``kept[r]`` becomes node
+    ``r``.  The last verified node ``v = path[k-1]`` becomes the root, and a
+    node's weight is the sum of values from the root down to it, so the kept
+    weights are re-based: ``cum'[r] = cum[kept[r]] - cum[v]``, the weight of
+    the path from the new root.  Entries at or past the new node count read
+    -1 (tok) and -inf (cum).  ``k = 0`` with ``keep`` changes nothing.
+    Returns ``(tok', cum')`` (``cum'`` None when ``cum`` is None); cum is
+    stored as float32, the difference taken in float64 and rounded once.
+    """
+    tok = np.asarray(tok, dtype=np.int32)
+    n_max = tok.shape[0]
+    if k == 0 and keep:
+        return tok.copy(), None if cum is None else np.asarray(cum, np.float32).copy()
+    v = [int(x) for x in path[:k]]
+    kept = descendants(parent, v[-1], n) if (keep and k > 0) else []
+    tok2 = np.full(n_max, -1, dtype=np.int32)
+    for r, u in enumerate(kept):
+        tok2[r] = tok[u]
+    if cum is None:
+        return tok2, None
+    cum = np.asarray(cum, dtype=np.float32)
+    cum2 = np.full(n_max, -np.inf, dtype=np.float32)
+    for r, u in enumerate(kept):
+        cum2[r] = np.float32(np.float64(cum[u]) - np.float64(cum[v[-1]]))
+    return tok2, cum2

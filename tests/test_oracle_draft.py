@@ -138,3 +138,61 @@ def test_select_ties_stay_a_subtree():
             assert all(depth[v] >= cut for v in range(n) if v not in s)
             last = sorted(v for v in range(n) if depth[v] == cut)
             assert sorted(v for v in s if depth[v] == cut) == last[:len([v for v in s if depth[v] == cut])]
+
+
+def test_fig2_reroot_moves_tokens_with_the_nodes(golden):
+    """Figure 2, iteration 1: after re-rooting at t6 the draft's next tree is
+    t9..t12 (their tokens in that order); iteration 2: t16 is outside the
+    tree, nothing is kept."""
+    fx = golden("fig2_iterations.json")
+    toks = fx["tree_tokens"]
+    idx = {t: i for i, t in enumerate(toks)}
+    n = len(toks)
+    par = np.full(n, -1, dtype=np.int32)
+    par[idx["t6"]] = idx["t3"]
+    for t in fx["under_t6"]:
+        par[idx[t]] = idx["t6"]
+    tok = np.array([_tok_id(t) for t in toks], dtype=np.int32)
+    path = [idx[t] for t in fx["iter1"]["path"]]
+    tok1, _ = oracle.reroot_node_arrays(par, n, path, len(path), True, tok)
+    m = len(fx["iter1"]["expected_tree"])
+    assert tok1[:m].tolist() == [_tok_id(t) for t in fx["iter1"]["expected_tree"]]
+    assert (tok1[m:] == -1).all()
+    _, _, par1, n1 = oracle.tree_cache_reroot([], np.array([5]), par[None], np.array([n]),
+                                              np.array([path + [-1] * (n - 2)]),
+                                              np.array([2]), np.array([True]))
+    p2, keep2 = oracle.token_walk(par1[0], tok1, int(n1[0]), [9, 16])
+    tok2, _ = oracle.reroot_node_arrays(par1[0], int(n1[0]), p2, len(p2), keep2, tok1)
+    assert keep2 is False and (tok2 == -1).all()
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_reroot_rebases_weights_to_the_new_root(seed):
+    """Re-rooting commutes with the definition of the weights: the weights of
+    the re-rooted tree, computed from scratch with the new root's own
+    distribution (the old row of the last verified node) and the kept nodes'
+    rows in their new order, equal the re-based, moved weights."""
+    rng = np.random.default_rng(300 + seed)
+    n, V = int(rng.integers(2, 14)), 7
+    par, tok = _random_tree(rng, n, V)
+    root_row = rng.standard_normal(V + n)
+    rows = rng.standard_normal((n, V + n))
+    cum = oracle.cumulative_scores(par, tok, root_row, rows, n).astype(np.float32)
+    end = int(rng.integers(0, n))
+    path = oracle.root_path(par, end)
+    k = int(rng.integers(1, len(path) + 1))
+    tok2, cum2 = oracle.reroot_node_arrays(par, n, path, k, True, tok, cum)
+    _, _, par2, n2 = oracle.tree_cache_reroot([], np.array([0]), par[None], np.array([n]),
+                                              np.array([path + [-1] * (n - len(path))]),
+                                              np.array([k]), np.array([True]))
+    n2 = int(n2[0])
+    kept = oracle.descendants(par, path[k - 1], n)
+    assert n2 == len(kept) and tok2[:n2].tolist() == [int(tok[u]) for u in kept]
+    fresh = oracle.cumulative_scores(par2[0], tok2, rows[path[k - 1]], rows[kept], n2)
+    np.testing.assert_allclose(cum2[:n2], fresh, rtol=2e-6, atol=2e-6)
+    assert np.all(np.isneginf(cum2[n2:])) and np.all(tok2[n2:] == -1)
+    # dropping the tree (no keep) leaves nothing; k = 0 with keep changes nothing
+    t3, c3 = oracle.reroot_node_arrays(par, n, path, k, False, tok, cum)
+    assert (t3 == -1).all() and np.all(np.isneginf(c3))
+    t4, c4 = oracle.reroot_node_arrays(par, n, path, 0, True, tok, cum)
+    assert np.array_equal(t4, tok) and np.array_equal(c4, cum)
