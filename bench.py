@@ -31,9 +31,10 @@ Other workloads (``--workload``), each printing the same kind of line:
                      leaves on the device (tree_expand_top_w over the root's
                      and every node's 32000-way distribution) and attends them
                      (tree_attn_expand), on KV copy s mod 64 (563 MB in all);
-                     then the walk along the verified tokens and the choice of
-                     the bs = 8 nodes to send (tree_token_walk,
-                     tree_select_subtree).
+                     then the walk along the verified tokens, the re-root of
+                     the KV rows, tokens and weights, and the choice of the
+                     bs = 8 nodes to send (tree_token_walk,
+                     tree_cache_reroot_draft, tree_select_subtree).
 
 Prints one JSON line (metric, value = microseconds per step, roofline of the
 attention call, CPU-oracle baseline on a bounded sample).
@@ -59,6 +60,7 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD's published peak
 METRIC = "tree-verify attention µs/step + achieved KV-read GB/s (% of MI355X HBM peak)"
 WORKLOADS = ("chain_verify", "paged_alternating", "tree_verify_l70b", "draft_expand")
 PHASE_REPS = 5                  # timed replays of each single-phase graph
+MIN_TIMED_CALLS = 50            # individually timed calls per phase (per-call percentiles)
 
 
 def _log(msg):
@@ -380,19 +382,27 @@ class TreeVerifyL70b(_Workload):
 
 
 class DraftExpand(_Workload):
-    """Four expansion rounds over a 64-node draft tree, all on the device: each
-    round tree_expand_top_w appends the w = 8 best leaves (maximum-likelihood
+    """One draft-side iteration over a 64-node draft tree, all on the device
+    (SwiftSpec summary, Section 3.1.1 Algorithm 1).  Four expansion rounds:
+    tree_expand_top_w appends the w = 8 best leaves (maximum-likelihood
     expansion over the 32000-way rows of the root and every node), then
-    tree_attn_expand attends the new leaves over prefix + tree.  Then the
-    draft side of the iteration: tree_token_walk along the target's verified
-    tokens (a root path of the grown tree, fixed once the first step has run)
-    and tree_select_subtree of the bs = 8 nodes to send.  The tree is restored
-    after the step (one elementwise kernel), so every step grows the same
-    tree.  Phases (HIP-graph mode): "expand" = the 4 attention calls, on the
-    trees the rounds produce; "topw" = one restore + the 4 selections;
-    "walk_select" = the walk and the selection on the grown tree.  With
-    --eager the phases are not separated (the whole step is "expand")."""
-    phases = ("expand", "topw", "walk_select")
+    tree_attn_expand attends the new leaves over prefix + tree.  Then
+    tree_token_walk along the target's verified tokens, tree_cache_reroot_draft
+    (the walked path joins the prefix, the subtree under its last node moves
+    forward with its KV rows, tokens and re-based weights) and
+    tree_select_subtree of the bs = 8 nodes to send, on the re-rooted tree.
+    The verified tokens are the root path of the grown tree's node at depth
+    >= 2 with the largest subtree (so the re-root keeps a subtree), fixed once
+    the first step has run.  The tree state (parents, tokens, weights, sizes,
+    prefix length) is restored after the step by one elementwise kernel, so
+    every step grows the same tree; the rows the re-root moved stay moved in
+    that step's KV copy (a permutation of tree rows, which changes no later
+    step's work).  Phases (HIP-graph mode): "expand" = the 4 attention calls,
+    on the trees the rounds produce; "topw" = one restore + the 4 selections;
+    "walk_reroot_select" = one copy of the grown tree's state, then the walk,
+    the re-root and the selection.  With --eager the phases are not separated
+    (the whole step is "expand")."""
+    phases = ("expand", "topw", "walk_reroot_select")
     COPIES = 64
     BS = 8       # nodes sent to the target per iteration
     M_VER = 8    # room for the verified tokens
@@ -415,27 +425,27 @@ class DraftExpand(_Workload):
         for r in range(e.rounds):
             lg[0, e.n0 + 1 + r * e.w:e.n0 + 1 + (r + 1) * e.w] = e.logits_new[r]
         self.logits = up(lg)
-        # tree state in one int32 buffer (parent, tok, cum bits, n) so that one
-        # kernel restores it
+        # tree state in one int32 buffer (parent, tok, cum bits, n, prefix
+        # length) so that one kernel restores it
         par = np.full(nm, -1, dtype=np.int32)
-        tok = np.zeros(nm, dtype=np.int32)
-        cum = np.zeros(nm, dtype=np.float32)
+        tok = np.full(nm, -1, dtype=np.int32)
+        cum = np.full(nm, -np.inf, dtype=np.float32)
         par[:e.n0], tok[:e.n0] = e.parent0, e.tok0
         cum[:e.n0] = self._cum0(e)
-        meta = np.concatenate([par, tok, cum.view(np.int32), np.array([e.n0], np.int32)])
+        meta = np.concatenate([par, tok, cum.view(np.int32), np.array([e.n0, e.P], np.int32)])
         self.meta0 = up(meta)
         self.meta = self.meta0.clone()
+        self.meta_grown = None
         self.par = self.meta[0:nm].view(1, nm)
         self.tok = self.meta[nm:2 * nm].view(1, nm)
         self.cum = self.meta[2 * nm:3 * nm].view(torch.float32).view(1, nm)
         self.n = self.meta[3 * nm:3 * nm + 1]
-        self.P = up(np.array([e.P], np.int32))
+        self.P = self.meta[3 * nm + 1:3 * nm + 2]
         self.qs = [up(e.q_new[r], True) for r in range(e.rounds)]
         self.outs = [torch.empty_like(q) for q in self.qs]
         self.lses = [torch.empty((1, e.Hq, e.w), dtype=torch.float32, device=up.dev)
                      for _ in self.qs]
         self.snaps = None   # per-round (parent, n) after its selection, for the expand phase
-        self.final = None   # (parent, tok, cum, n) of the grown tree
         i32 = dict(dtype=torch.int32, device=up.dev)
         self.verified = torch.zeros((1, self.M_VER), **i32)
         self.vlen = torch.zeros((1,), **i32)
@@ -452,8 +462,8 @@ class DraftExpand(_Workload):
                        "w": e.w, "rounds": e.rounds, "vocab": e.vocab, "kv_copies": self.COPIES,
                        "bs": self.BS,
                        "step": "4 rounds of top-w selection + expansion attention, then the walk "
-                               "along the verified tokens and the size-bs subtree selection "
-                               "(+ tree restore)"}
+                               "along the verified tokens, the re-root (KV, tokens, weights) "
+                               "and the size-bs subtree selection (+ tree restore)"}
 
     @staticmethod
     def _cum0(e):
@@ -479,12 +489,15 @@ class DraftExpand(_Workload):
         self.ta.tree_attn_expand(self.qs[r], kv, self.P, self.par, self.n, self.e.scale,
                                  out=self.outs[r], lse=self.lses[r], workspace=ws, **opts)
 
-    def _restore(self):
-        self.torch.add(self.meta0, 0, out=self.meta)
+    def _restore(self, src=None):
+        self.torch.add(self.meta0 if src is None else src, 0, out=self.meta)
 
-    def _draft_side(self, par, tok, cum, n):
-        self.ta.tree_token_walk(par, tok, n, self.verified, self.vlen, *self.walk_out)
-        self.ta.tree_select_subtree(cum, par, tok, n, self.BS, *self.sel_out)
+    def _draft_side(self, kv):
+        path, plen, keep = self.walk_out
+        self.ta.tree_token_walk(self.par, self.tok, self.n, self.verified, self.vlen, *self.walk_out)
+        self.ta.tree_cache_reroot_draft([kv], self.P, self.par, self.n, path, plen, keep,
+                                        self.tok, self.cum)
+        self.ta.tree_select_subtree(self.cum, self.par, self.tok, self.n, self.BS, *self.sel_out)
 
     def step(self, i, ws, marks, opts):
         kv = self.kvs[i % self.COPIES]
@@ -492,14 +505,15 @@ class DraftExpand(_Workload):
             marks[0].record()
         for r in range(self.e.rounds):
             self._round(r, kv, ws, opts)
-        self._draft_side(self.par, self.tok, self.cum, self.n)
+        self._draft_side(kv)
         self._restore()
         if marks is not None:
             marks[1].record()
             marks[2].record()
 
     def _snapshots(self, ws, opts):
-        """Each round's tree after its selection (from one eager pass)."""
+        """Each round's tree after its selection, and the grown tree's whole
+        state (from one eager pass)."""
         torch = self.torch
         self._restore()
         snaps = []
@@ -507,7 +521,7 @@ class DraftExpand(_Workload):
             self.ta.tree_expand_top_w(self.logits, self.par, self.tok, self.cum, self.n,
                                       self.e.w, workspace=self.topw_ws)
             snaps.append((self.par.clone(), self.n.clone()))
-        self.final = (self.par.clone(), self.tok.clone(), self.cum.clone(), self.n.clone())
+        self.meta_grown = self.meta.clone()
         self._restore()
         torch.cuda.synchronize()
         return snaps
@@ -526,7 +540,8 @@ class DraftExpand(_Workload):
                 self.ta.tree_expand_top_w(self.logits, self.par, self.tok, self.cum, self.n,
                                           self.e.w, workspace=self.topw_ws)
         else:
-            self._draft_side(*self.final)
+            self._restore(self.meta_grown)
+            self._draft_side(kv)
 
     def attn_bytes(self, i):
         return self.bytes
@@ -545,16 +560,24 @@ class DraftExpand(_Workload):
 
     def _set_verified(self):
         """The target's verified tokens: the root path of the grown tree's
-        best node (largest cumulative score) at depth 4 or less."""
-        import numpy as np
-
-        import oracle
-        par, tok, cum, n = (t.cpu().numpy() for t in self.final)
-        n = int(n[0])
-        par, tok, cum = par[0], tok[0], cum[0]
-        cand = [i for i in range(n) if oracle.depth(par, i) <= min(4, self.M_VER)]
-        best = max(cand, key=lambda i: (float(cum[i]), -i))
-        ver = [int(tok[v]) for v in oracle.root_path(par, best)]
+        node at depth >= 2 with the largest subtree (lowest index on ties), so
+        that the walk keeps that subtree.  Plain loops over the parent array."""
+        nm = self.e.n_max
+        g = self.meta_grown.cpu().numpy()
+        par, tok, n = g[0:nm], g[nm:2 * nm], int(g[3 * nm])
+        depth, size = [0] * n, [1] * n
+        for i in range(n):
+            depth[i] = 1 + (depth[par[i]] if par[i] >= 0 else 0)
+        for i in range(n - 1, -1, -1):
+            if par[i] >= 0:
+                size[par[i]] += size[i]
+        cand = [i for i in range(n) if 2 <= depth[i] <= self.M_VER]
+        x = max(cand, key=lambda i: (size[i], -i))
+        ver = []
+        while x >= 0:
+            ver.append(int(tok[x]))
+            x = int(par[x])
+        ver.reverse()
         self.verified.zero_()
         self.verified[0, :len(ver)] = self.torch.tensor(ver, dtype=self.torch.int32)
         self.vlen.fill_(len(ver))
@@ -583,13 +606,20 @@ class DraftExpand(_Workload):
             oracle.expand(oc, e.q_new[r], e.w)
             rows = np.concatenate([rows, e.logits_new[r]])
         ver = self.verified[0, :int(self.vlen.item())].cpu().numpy()
-        oracle.token_walk(par, tok, n, ver)
-        oracle.select_subtree(par, tok, oracle.cumulative_scores(par, tok, e.logits_root, rows[:n], n),
-                              n, self.BS)
+        path, keep = oracle.token_walk(par, tok, n, ver)
+        cum = oracle.cumulative_scores(par, tok, e.logits_root, rows[:n], n)
+        pth = np.full((1, e.n_max), -1, dtype=np.int32)
+        pth[0, :len(path)] = path
+        _, _, par2, n2 = oracle.tree_cache_reroot([(e.k, e.v)], np.array([e.P]), par[None],
+                                                  np.array([n]), pth, np.array([len(path)]),
+                                                  np.array([keep]))
+        tok2, cum2 = oracle.reroot_node_arrays(par, n, path, len(path), keep, tok,
+                                               cum.astype(np.float32))
+        oracle.select_subtree(par2[0], tok2, cum2, int(n2[0]), self.BS)
         dt = time.perf_counter() - t0
         return {"value": dt * 1e6, "unit": "us/step", "cores": _blas_threads(), "kind": "oracle",
                 "sample": "all 4 rounds of one step (top-w selection + expansion attention) "
-                          "and the walk + subtree selection",
+                          "and the walk, re-root and subtree selection",
                 "host_cpus": len(os.sched_getaffinity(0))}
 
     def c_like(self):
@@ -629,7 +659,7 @@ def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", choices=WORKLOADS, default="chain_verify")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -697,6 +727,7 @@ def main(argv=None):
         torch.cuda.synchronize()
         ms_per_step = start.elapsed_time(stop) / a.steps
         phase_ms = [[m[j].elapsed_time(m[j + 1]) for m in marks] for j in range(nph)]
+        call_ms = phase_ms[0]
     else:
         # The K steps are captured once in a HIP graph (every size the kernels
         # need is in device memory) and replayed: the timed region is the
@@ -707,6 +738,29 @@ def main(argv=None):
             with torch.cuda.graph(g):
                 fn()
             return g
+
+        def time_single_calls(fn_of_i, lead_graph, est_ms):
+            """Durations (ms) of at least MIN_TIMED_CALLS single calls, each
+            issued from Python between two events.  At least 10 ms of the same
+            calls (replays of the phase's graph) are queued first, so the host
+            has issued every timed call before the device reaches it: the
+            intervals hold device time (plus the ~1 us of the events), not
+            host launch latency, and the clocks are those of sustained work.
+            (One-call graphs would add ~8 us of graph launch per call; a
+            device-side spin as the lead lowers the clocks of the work after
+            it.)"""
+            n = max(MIN_TIMED_CALLS, len(steps))
+            marks = [(ev(), ev()) for _ in range(n)]
+            lead = max(1, int(np.ceil(10.0 / max(est_ms * len(steps), 1e-3))))
+            torch.cuda.synchronize()
+            for _ in range(lead):
+                lead_graph.replay()
+            for c, (e0, e1) in enumerate(marks):
+                e0.record()
+                fn_of_i(steps[c % len(steps)])
+                e1.record()
+            torch.cuda.synchronize()
+            return [e0.elapsed_time(e1) for e0, e1 in marks]
 
         g_steps = capture(lambda: [w.step(i, ws, None, opts) for i in steps])
         g_steps.replay()
@@ -734,6 +788,9 @@ def main(argv=None):
                 torch.cuda.synchronize()
                 per_call.append(e0.elapsed_time(e1) / a.steps)
             phase_ms.append(per_call)
+            if j == 0:
+                call_ms = time_single_calls(lambda i: w.phase(i, 0, ws, opts), g,
+                                            float(np.mean(per_call)))
             del g
         # Calls timed beside the step (not part of it), the same way, last:
         # they may rewrite the inputs.
@@ -787,9 +844,11 @@ def main(argv=None):
                   "hip_graph (the K steps captured once, replayed)",
         "kv_read_GBps": round(kv_gbps, 1),
         "pct_hbm_peak": round(100 * kv_gbps / HBM_PEAK_GBPS, 2),
-        f"{w.phases[0]}_us": {"median": round(med(attn_ms) * 1e3, 2),
-                              "p10": round(pct(attn_ms, 10) * 1e3, 2),
-                              "p90": round(pct(attn_ms, 90) * 1e3, 2)},
+        f"{w.phases[0]}_us": {"median": round(med(call_ms) * 1e3, 2),
+                              "p10": round(pct(call_ms, 10) * 1e3, 2),
+                              "p90": round(pct(call_ms, 90) * 1e3, 2),
+                              "calls": len(call_ms),
+                              "mean_in_step_graph": round(float(np.mean(attn_ms)) * 1e3, 2)},
     }
     for j in range(1, nph):
         res[f"{w.phases[j]}_us"] = round(med(phase_ms[j]) * 1e3, 2)
@@ -801,6 +860,15 @@ def main(argv=None):
     res["roofline"] = roofline
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = w.cpu_baseline(a.cpu_budget)
+        # the same oracle on one core (BLAS limited to one thread)
+        try:
+            from threadpoolctl import threadpool_limits
+        except ImportError:  # pragma: no cover
+            threadpool_limits = None
+        if threadpool_limits is not None:
+            with threadpool_limits(limits=1):
+                one = w.cpu_baseline(a.cpu_budget)
+            res["cpu_baseline_1core"] = one
     print(json.dumps(res), flush=True)
 
 

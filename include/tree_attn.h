@@ -190,6 +190,31 @@ int tree_cache_reroot(const ta_kv* kv_layers, int n_layers, int32_t* prefix_len,
                       void* stream);
 
 /*
+ * Draft-side re-root ([SS] Section 3.1.1 Algorithm 1: Re-root, then Select
+ * on the re-rooted tree; Section 3.2 update procedure; Section 3.1.3: a
+ * node's weight is the sum of values from the root down to it).  Exactly
+ * tree_cache_reroot, and with the same node mapping the per-node arrays the
+ * draft keeps beside its tree:
+ *
+ *   tok [B][n_max] int32 in/out: node tokens (required); kept node number r
+ *            (in original order) takes the token of the node it was
+ *   cum [B][n_max] fp32 in/out (may be NULL): cumulative log-probabilities
+ *            (as tree_expand_top_w keeps them), re-based to the new root, the
+ *            last verified node v: cum'[r] = cum[kept node r] - cum[v], one
+ *            fp32 subtraction
+ *
+ * Entries at or past the new n_nodes[b] are set to -1 (tok) and -inf (cum).
+ * k == 0 with keep changes nothing; k == 0 without keep, or a path whose
+ * last node has no descendants, leaves no node.  The draft's next
+ * tree_expand_top_w and tree_select_subtree then read a consistent tree.
+ */
+int tree_cache_reroot_draft(const ta_kv* kv_layers, int n_layers, int32_t* prefix_len,
+                            int32_t* parent, int32_t* n_nodes, const int32_t* path,
+                            const int32_t* path_len, const uint8_t* keep_subtree, int32_t* tok,
+                            float* cum, int B, int n_max, int Hkv, int d, int dtype,
+                            void* stream);
+
+/*
  * Tree verification by speculative sampling, temperature > 0 ([MD] the
  * PEARL walkthrough: a rejected draft token is replaced by a draw from
  * norm(max(0, p - q)); [MD] experimental setup: sampling at temperature

@@ -259,3 +259,24 @@ def test_workspace_reuse_across_plans(ta):
             Or, Lr = oracle.verify(c)
             assert_attn_close(to_f64(out), lse.cpu().numpy(), Or, Lr, "bf16",
                               what=f"rep {rep} case {i}")
+
+
+def test_default_workspace_is_per_stream(ta):
+    """Calls on two streams without an explicit workspace get one workspace
+    each (so they cannot race on partial results) and the same outputs."""
+    import torch
+    from tree_masked_verify_attn_amd import _lib
+    c = random_case(77, B=3, Hq=16, Hkv=2, d=128, P_range=(3000, 5000), n_max=8, dtype="bf16")
+    dc = DevCase(c)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s1):
+        o1, l1 = ta.tree_attn_verify(dc.q, dc.kv, dc.prefix_len, dc.parent, dc.n_nodes, c.scale)
+    with torch.cuda.stream(s2):
+        o2, l2 = ta.tree_attn_verify(dc.q, dc.kv, dc.prefix_len, dc.parent, dc.n_nodes, c.scale)
+    torch.cuda.synchronize()
+    keys = {k for k in _lib._default_ws if k[1] in (s1.cuda_stream, s2.cuda_stream)}
+    assert len(keys) == 2
+    bufs = [_lib._default_ws[k].buf for k in keys]
+    assert bufs[0].data_ptr() != bufs[1].data_ptr()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)

@@ -36,6 +36,7 @@ EXPORTED_SYMBOLS = (
     "accept_sampling_path",
     "accept_sampling_workspace_bytes",
     "tree_cache_reroot",
+    "tree_cache_reroot_draft",
     "tree_expand_top_w",
     "tree_expand_top_w_workspace_bytes",
     "tree_rope_append",
@@ -113,6 +114,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.tree_cache_reroot.argtypes = [ctypes.POINTER(ta_kv), c_int, vp, vp, vp, vp, vp, vp,
                                           c_int, c_int, c_int, c_int, c_int, vp]
         lib.tree_cache_reroot.restype = c_int
+        lib.tree_cache_reroot_draft.argtypes = [ctypes.POINTER(ta_kv), c_int] + [vp] * 8 + \
+            [c_int] * 5 + [vp]
+        lib.tree_cache_reroot_draft.restype = c_int
         lib.tree_expand_top_w.argtypes = [vp, c_int, vp, vp, vp, vp, c_int, c_int, c_int, c_int,
                                           vp, c_size, vp]
         lib.tree_expand_top_w.restype = c_int
@@ -263,9 +267,12 @@ class Workspace:
         self.device = device
         self.buf = None
 
-    def get(self, nbytes: int, device=None):
+    def get(self, nbytes: int, device=None, stream=None):
         """The buffer (at least ``nbytes``) on ``device`` (default: the one given at
-        construction); always device memory, never host memory."""
+        construction); always device memory, never host memory.  ``stream``
+        (a torch stream) is the stream the call runs on: a buffer that is
+        replaced is marked as used there, so that the caching allocator does
+        not hand its memory out while a queued kernel may still read it."""
         torch = _torch()
         if nbytes == 0:
             return None
@@ -275,19 +282,33 @@ class Workspace:
         if dev.index is None:
             dev = torch.device("cuda", torch.cuda.current_device())
         if self.buf is None or self.buf.numel() < nbytes or self.buf.device != dev:
+            if self.buf is not None and stream is not None and self.buf.device == dev:
+                self.buf.record_stream(stream)
             self.buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)
         return self.buf
 
 
+# Implicit workspaces, one per (device, stream): calls on different streams
+# never share one.
 _default_ws = {}
 
 
-def _workspace_for(device, nbytes):
-    key = str(device)
+def _torch_stream(stream, device):
+    torch = _torch()
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    if hasattr(stream, "cuda_stream"):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=device)
+
+
+def _workspace_for(device, nbytes, stream=None):
+    ts = _torch_stream(stream, device)
+    key = (str(device), int(ts.cuda_stream))
     ws = _default_ws.get(key)
     if ws is None:
         ws = _default_ws[key] = Workspace(device)
-    return ws.get(nbytes)
+    return ws.get(nbytes, stream=ts)
 
 
 def _attention(fn_name, q, kv: KVCache, prefix_len, parent, n_nodes, scale, out, lse, workspace,
@@ -336,9 +357,10 @@ def _attention(fn_name, q, kv: KVCache, prefix_len, parent, n_nodes, scale, out,
         return out, lse
     nbytes = tree_attn_workspace_bytes(B, n_q, Hq, kv.Hkv, d, dt, kv.T_cap, chunk_tokens, kernel)
     if workspace is None:
-        ws = _workspace_for(dev, nbytes)
+        ws = _workspace_for(dev, nbytes, stream)
     else:
-        ws = workspace.get(nbytes, dev) if isinstance(workspace, Workspace) else workspace
+        ws = (workspace.get(nbytes, dev, _torch_stream(stream, dev))
+              if isinstance(workspace, Workspace) else workspace)
     if ws is not None:
         _need(ws, "workspace", device=dev)   # device memory of this call's GPU only
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
@@ -459,9 +481,10 @@ def accept_sampling_path(target_logits, draft_logits, parent, tok, n_nodes, root
         raise ValueError("path must be [B][n_max], path_len and bonus [B]")
     nbytes = accept_sampling_workspace_bytes(B, n_max)
     if workspace is None:
-        ws = _workspace_for(dev, nbytes)
+        ws = _workspace_for(dev, nbytes, stream)
     else:
-        ws = workspace.get(nbytes, dev) if isinstance(workspace, Workspace) else workspace
+        ws = (workspace.get(nbytes, dev, _torch_stream(stream, dev))
+              if isinstance(workspace, Workspace) else workspace)
     if ws is not None:
         _need(ws, "workspace", device=dev)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
@@ -475,9 +498,8 @@ def accept_sampling_path(target_logits, draft_logits, parent, tok, n_nodes, root
     return path, path_len, bonus
 
 
-def tree_cache_reroot(kv_layers: Sequence[KVCache], prefix_len, parent, n_nodes, path, path_len,
-                      keep_subtree, stream=None):
-    """In-place re-root of every layer's cache and of prefix_len/parent/n_nodes."""
+def _reroot(kv_layers, prefix_len, parent, n_nodes, path, path_len, keep_subtree, tok, cum,
+            stream, draft):
     torch = _torch()
     lib = load_library()
     dev = parent.device
@@ -488,6 +510,14 @@ def tree_cache_reroot(kv_layers: Sequence[KVCache], prefix_len, parent, n_nodes,
     _need(path_len, "path_len", dtype=torch.int32, ndim=1, device=dev)
     _need(keep_subtree, "keep_subtree", dtype=torch.uint8, ndim=1, device=dev)
     B, n_max = (int(x) for x in parent.shape)
+    if draft:
+        _need(tok, "tok", dtype=torch.int32, ndim=2, device=dev)
+        if tuple(tok.shape) != (B, n_max):
+            raise ValueError("tok must be [B][n_max] like parent")
+        if cum is not None:
+            _need(cum, "cum", dtype=torch.float32, ndim=2, device=dev)
+            if tuple(cum.shape) != (B, n_max):
+                raise ValueError("cum must be [B][n_max] like parent")
     layers: List[KVCache] = list(kv_layers)
     if layers:
         Hkv, d, dtype = layers[0].Hkv, layers[0].d, layers[0].dtype
@@ -498,10 +528,29 @@ def tree_cache_reroot(kv_layers: Sequence[KVCache], prefix_len, parent, n_nodes,
     else:
         Hkv, d, dt = 1, 128, TA_BF16
     arr = (ta_kv * max(1, len(layers)))(*[L.struct() for L in layers])
-    st = lib.tree_cache_reroot(arr, len(layers), prefix_len.data_ptr(), parent.data_ptr(),
-                               n_nodes.data_ptr(), path.data_ptr(), path_len.data_ptr(),
-                               keep_subtree.data_ptr(), B, n_max, Hkv, d, dt, _stream(stream))
+    head = (arr, len(layers), prefix_len.data_ptr(), parent.data_ptr(), n_nodes.data_ptr(),
+            path.data_ptr(), path_len.data_ptr(), keep_subtree.data_ptr())
+    if draft:
+        st = lib.tree_cache_reroot_draft(*head, tok.data_ptr(), _ptr(cum), B, n_max, Hkv, d, dt,
+                                         _stream(stream))
+    else:
+        st = lib.tree_cache_reroot(*head, B, n_max, Hkv, d, dt, _stream(stream))
     _check(st)
+
+
+def tree_cache_reroot(kv_layers: Sequence[KVCache], prefix_len, parent, n_nodes, path, path_len,
+                      keep_subtree, stream=None):
+    """In-place re-root of every layer's cache and of prefix_len/parent/n_nodes."""
+    _reroot(kv_layers, prefix_len, parent, n_nodes, path, path_len, keep_subtree, None, None,
+            stream, False)
+
+
+def tree_cache_reroot_draft(kv_layers: Sequence[KVCache], prefix_len, parent, n_nodes, path,
+                            path_len, keep_subtree, tok, cum=None, stream=None):
+    """tree_cache_reroot that also moves the draft's per-node tokens ``tok``
+    and (re-based to the new root) cumulative scores ``cum``, in place."""
+    _reroot(kv_layers, prefix_len, parent, n_nodes, path, path_len, keep_subtree, tok, cum,
+            stream, True)
 
 
 def tree_expand_top_w_workspace_bytes(B: int, n_max: int, w: int) -> int:
@@ -537,9 +586,10 @@ def tree_expand_top_w(logits, parent, tok, cum, n_nodes, w: int, workspace=None,
         raise ValueError("n_nodes must be [B]")
     nbytes = tree_expand_top_w_workspace_bytes(B, n_max, int(w))
     if workspace is None:
-        ws = _workspace_for(dev, nbytes)
+        ws = _workspace_for(dev, nbytes, stream)
     else:
-        ws = workspace.get(nbytes, dev) if isinstance(workspace, Workspace) else workspace
+        ws = (workspace.get(nbytes, dev, _torch_stream(stream, dev))
+              if isinstance(workspace, Workspace) else workspace)
     if ws is not None:
         _need(ws, "workspace", device=dev)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()

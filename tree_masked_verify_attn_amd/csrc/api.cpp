@@ -151,6 +151,44 @@ int check_kv(const ta_kv& kv) {
   return TA_OK;
 }
 
+// tree_cache_reroot and its draft-side variant: the move launches (groups of
+// layers), then the metadata launch (which also moves tok / cum when given).
+int reroot_call(const ta_kv* kv_layers, int n_layers, int32_t* prefix_len, int32_t* parent,
+                int32_t* n_nodes, const int32_t* path, const int32_t* path_len,
+                const uint8_t* keep_subtree, int32_t* tok, float* cum, int B, int n_max, int Hkv,
+                int d, int dtype, void* stream) {
+  if (B < 0 || n_layers < 0 || n_max < 1 || Hkv < 1) return TA_ERR_INVALID_ARG;
+  if (n_max > TA_MAX_NODES) return TA_ERR_TREE_TOO_LARGE;
+  if (dtype != TA_F32 && dtype != TA_BF16) return TA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return TA_ERR_UNSUPPORTED;
+  if (prefix_len == nullptr || parent == nullptr || n_nodes == nullptr || path == nullptr ||
+      path_len == nullptr || keep_subtree == nullptr || (n_layers > 0 && kv_layers == nullptr))
+    return TA_ERR_INVALID_ARG;
+  for (int i = 0; i < n_layers; ++i) {
+    const int st = check_kv(kv_layers[i]);
+    if (st != TA_OK) return st;
+    if (!aligned16(kv_layers[i].k) || !aligned16(kv_layers[i].v)) return TA_ERR_INVALID_ARG;
+  }
+  if (B == 0) return TA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int row_bytes = d * (dtype == TA_BF16 ? 2 : 4);
+  for (int l0 = 0; l0 < n_layers; l0 += ta::kRerootMaxLayersPerLaunch) {
+    const int cnt = std::min(ta::kRerootMaxLayersPerLaunch, n_layers - l0);
+    ta::RerootLayers L{};
+    for (int i = 0; i < cnt; ++i) {
+      const ta_kv& kv = kv_layers[l0 + i];
+      L.l[i] = ta::RerootLayer{kv.k, kv.v, kv.block_table, kv.block_size, kv.max_blocks,
+                               kv.num_blocks, kv.T_cap};
+    }
+    hipError_t e = ta::launch_reroot_move(L, cnt, prefix_len, parent, n_nodes, path, path_len,
+                                          keep_subtree, B, n_max, Hkv, row_bytes, s);
+    if (e != hipSuccess) return hip_status(e, "tree_cache_reroot move launch");
+  }
+  hipError_t e = ta::launch_reroot_meta(prefix_len, parent, n_nodes, path, path_len, keep_subtree,
+                                        B, n_max, tok, cum, s);
+  return hip_status(e, "tree_cache_reroot metadata launch");
+}
+
 }  // namespace
 
 namespace ta {
@@ -415,36 +453,18 @@ int tree_cache_reroot(const ta_kv* kv_layers, int n_layers, int32_t* prefix_len,
                       int32_t* n_nodes, const int32_t* path, const int32_t* path_len,
                       const uint8_t* keep_subtree, int B, int n_max, int Hkv, int d, int dtype,
                       void* stream) {
-  if (B < 0 || n_layers < 0 || n_max < 1 || Hkv < 1) return TA_ERR_INVALID_ARG;
-  if (n_max > TA_MAX_NODES) return TA_ERR_TREE_TOO_LARGE;
-  if (dtype != TA_F32 && dtype != TA_BF16) return TA_ERR_UNSUPPORTED;
-  if (d != 64 && d != 128) return TA_ERR_UNSUPPORTED;
-  if (prefix_len == nullptr || parent == nullptr || n_nodes == nullptr || path == nullptr ||
-      path_len == nullptr || keep_subtree == nullptr || (n_layers > 0 && kv_layers == nullptr))
-    return TA_ERR_INVALID_ARG;
-  for (int i = 0; i < n_layers; ++i) {
-    const int st = check_kv(kv_layers[i]);
-    if (st != TA_OK) return st;
-    if (!aligned16(kv_layers[i].k) || !aligned16(kv_layers[i].v)) return TA_ERR_INVALID_ARG;
-  }
-  if (B == 0) return TA_OK;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int row_bytes = d * (dtype == TA_BF16 ? 2 : 4);
-  for (int l0 = 0; l0 < n_layers; l0 += ta::kRerootMaxLayersPerLaunch) {
-    const int cnt = std::min(ta::kRerootMaxLayersPerLaunch, n_layers - l0);
-    ta::RerootLayers L{};
-    for (int i = 0; i < cnt; ++i) {
-      const ta_kv& kv = kv_layers[l0 + i];
-      L.l[i] = ta::RerootLayer{kv.k, kv.v, kv.block_table, kv.block_size, kv.max_blocks,
-                               kv.num_blocks, kv.T_cap};
-    }
-    hipError_t e = ta::launch_reroot_move(L, cnt, prefix_len, parent, n_nodes, path, path_len,
-                                          keep_subtree, B, n_max, Hkv, row_bytes, s);
-    if (e != hipSuccess) return hip_status(e, "tree_cache_reroot move launch");
-  }
-  hipError_t e = ta::launch_reroot_meta(prefix_len, parent, n_nodes, path, path_len, keep_subtree,
-                                        B, n_max, s);
-  return hip_status(e, "tree_cache_reroot metadata launch");
+  return reroot_call(kv_layers, n_layers, prefix_len, parent, n_nodes, path, path_len,
+                     keep_subtree, nullptr, nullptr, B, n_max, Hkv, d, dtype, stream);
+}
+
+int tree_cache_reroot_draft(const ta_kv* kv_layers, int n_layers, int32_t* prefix_len,
+                            int32_t* parent, int32_t* n_nodes, const int32_t* path,
+                            const int32_t* path_len, const uint8_t* keep_subtree, int32_t* tok,
+                            float* cum, int B, int n_max, int Hkv, int d, int dtype,
+                            void* stream) {
+  if (tok == nullptr) return TA_ERR_INVALID_ARG;
+  return reroot_call(kv_layers, n_layers, prefix_len, parent, n_nodes, path, path_len,
+                     keep_subtree, tok, cum, B, n_max, Hkv, d, dtype, stream);
 }
 
 size_t tree_expand_top_w_workspace_bytes(int B, int n_max, int w) {

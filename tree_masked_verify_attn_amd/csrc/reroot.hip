@@ -13,7 +13,8 @@
 // exclusively, a destination that is another move's source is never
 // overwritten before it has been read.
 // Launch 2 (metadata): one work group per sequence rewrites parent, n_nodes
-// and prefix_len after every layer has been moved (stream order).
+// and prefix_len after every layer has been moved (stream order), and moves
+// the draft's per-node tokens and weights when it is given them.
 #include "ta_device.h"
 
 namespace ta {
@@ -167,11 +168,16 @@ __global__ __launch_bounds__(kThreads) void reroot_move_kernel(
   store(3, r3);
 }
 
+// tok / cum (either may be null): per-node arrays the draft keeps beside its
+// tree.  They move with their nodes; cum is re-based to the new root (the last
+// verified node), whose own weight is subtracted.  Entries at or past the new
+// node count read -1 / -inf.
 __global__ __launch_bounds__(kThreads) void reroot_meta_kernel(int32_t* prefix_len,
                                                                int32_t* parent, int32_t* n_nodes,
                                                                const int32_t* path,
                                                                const int32_t* path_len,
-                                                               const uint8_t* keep, int n_max) {
+                                                               const uint8_t* keep, int n_max,
+                                                               int32_t* tok, float* cum) {
   __shared__ uint64_t sAnc[kMaxNodes][kMaskWords];
   __shared__ int sJump[kMaxNodes];
   __shared__ uint64_t sKept[kMaskWords];
@@ -179,19 +185,33 @@ __global__ __launch_bounds__(kThreads) void reroot_meta_kernel(int32_t* prefix_l
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   int32_t* par_b = parent + static_cast<size_t>(b) * n_max;
+  int32_t* tok_b = tok != nullptr ? tok + static_cast<size_t>(b) * n_max : nullptr;
+  float* cum_b = cum != nullptr ? cum + static_cast<size_t>(b) * n_max : nullptr;
   const Plan pl = make_plan(prefix_len, parent, n_nodes, path, path_len, keep, b, n_max, sAnc,
                             sJump, sKept, sPath);
   if (!pl.valid || (pl.k == 0 && pl.keep)) return;
-  // Read every old parent before any write.
-  int newpar = -1, slot = -1;
+  // Read every old parent, token and weight before any write.
+  int newpar = -1, slot = -1, tk = -1;
+  float w = 0.f;
+  const float base = (cum_b != nullptr && pl.v_last >= 0) ? cum_b[pl.v_last] : 0.f;
   if (tid < pl.n && mask_bit(sKept, tid)) {
     const int pp = clamp_parent(par_b[tid], tid);
     slot = kept_rank(sKept, tid);
     newpar = (pp == pl.v_last || pp < 0) ? -1 : kept_rank(sKept, pp);
+    if (tok_b != nullptr) tk = tok_b[tid];
+    if (cum_b != nullptr) w = cum_b[tid];
   }
   __syncthreads();
-  if (tid < n_max && tid >= pl.n_kept) par_b[tid] = -1;
-  if (slot >= 0) par_b[slot] = newpar;
+  if (tid < n_max && tid >= pl.n_kept) {
+    par_b[tid] = -1;
+    if (tok_b != nullptr) tok_b[tid] = -1;
+    if (cum_b != nullptr) cum_b[tid] = -INFINITY;
+  }
+  if (slot >= 0) {
+    par_b[slot] = newpar;
+    if (tok_b != nullptr) tok_b[slot] = tk;
+    if (cum_b != nullptr) cum_b[slot] = w - base;
+  }
   if (tid == 0) {
     prefix_len[b] = pl.P + pl.k;
     n_nodes[b] = pl.n_kept;
@@ -212,9 +232,9 @@ hipError_t launch_reroot_move(const RerootLayers& layers, int n_layers, const in
 
 hipError_t launch_reroot_meta(int32_t* prefix_len, int32_t* parent, int32_t* n_nodes,
                               const int32_t* path, const int32_t* path_len, const uint8_t* keep,
-                              int B, int n_max, hipStream_t s) {
+                              int B, int n_max, int32_t* tok, float* cum, hipStream_t s) {
   return launch(reroot_meta_kernel, dim3(B), dim3(kThreads), s, prefix_len, parent, n_nodes, path,
-                path_len, keep, n_max);
+                path_len, keep, n_max, tok, cum);
 }
 
 }  // namespace ta

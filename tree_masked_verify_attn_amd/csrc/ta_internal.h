@@ -165,6 +165,6 @@ hipError_t launch_reroot_move(const RerootLayers& layers, int n_layers,
                               int Hkv, int row_bytes, hipStream_t s);
 hipError_t launch_reroot_meta(int32_t* prefix_len, int32_t* parent, int32_t* n_nodes,
                               const int32_t* path, const int32_t* path_len, const uint8_t* keep,
-                              int B, int n_max, hipStream_t s);
+                              int B, int n_max, int32_t* tok, float* cum, hipStream_t s);
 
 }  // namespace ta
