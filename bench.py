@@ -260,9 +260,10 @@ class ChainVerify(_Workload):
 
     def extras(self):
         """RoPE at the tree positions and the KV append of the 16 nodes per
-        sequence (tree_rope_append), timed beside the step: the workload's
-        queries and tree keys stand in for un-rotated ones, and the rotated
-        keys overwrite the tree rows (so this runs after everything else)."""
+        sequence (tree_rope_append), and the verify call with RoPE fused in
+        (tree_attn_verify_rope), timed beside the step: the workload's queries
+        and tree keys stand in for un-rotated ones, and the rotated keys
+        overwrite the tree rows (so these run after everything else)."""
         import torch
         bt, c = self.batch, self.c
         if self._rope is None:
@@ -295,7 +296,15 @@ class ChainVerify(_Workload):
         def sampling(i, ws, opts):
             bt.ta.accept_sampling_path(bt.logits, dft, bt.par, bt.tok, bt.n, bt.root_tok, u, ub,
                                        1.0, *outs, workspace=ws_s)
-        return {"rope_append": rope, "accept_sampling": sampling}
+        out_r = torch.empty_like(bt.q)
+        lse_r = torch.empty((c.B, c.Hq, c.n_max), dtype=torch.float32, device=bt.q.device)
+
+        def verify_rope(i, ws, opts):
+            # the verify call with RoPE fused in (rotation on load, tree rows
+            # staged and written by the attention kernel)
+            bt.ta.tree_attn_verify_rope(bt.q, k_new, v_new, bt.kv, bt.P, bt.par, bt.n, c.scale,
+                                        out=out_r, lse=lse_r, workspace=ws, **opts)
+        return {"rope_append": rope, "accept_sampling": sampling, "verify_rope": verify_rope}
 
     def attn_bytes(self, i):
         return self.batch.bytes

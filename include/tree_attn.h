@@ -144,6 +144,43 @@ int tree_attn_expand(const void* q, ta_kv kv, const int32_t* prefix_len, const i
                      const ta_attn_opts* opts, void* stream);
 
 /*
+ * Verification / expansion attention with the position embedding fused in
+ * ([SS] Section 3.3: the masked-attention kernel takes RoPE; Section 3.2: a
+ * node's KV is written once, where it was computed).  The same results, and
+ * the same cache rows written, as tree_rope_append(q, q_rot, k_new, v_new, kv,
+ * ...) followed by tree_attn_verify / tree_attn_expand on q_rot, in one call:
+ *
+ *   q             [B][n_q][Hq][d] (dtype) un-rotated queries (n_q = n_max for
+ *                 verify, w for expand; slot s holds node s, or node
+ *                 n_nodes[b] - w + s when expanding)
+ *   k_new, v_new  [B][n_q][Hkv][d] (dtype) the same slots' un-rotated keys and
+ *                 their values; the call rotates the keys to the nodes'
+ *                 positions P - 1 + depth and writes keys and values to cache
+ *                 rows P + node, as tree_rope_append does
+ *   base          RoPE base (> 0, finite): channel pair (j, j + d/2) turns by
+ *                 position * base^(-2j/d)
+ *   everything else as for tree_attn_verify / tree_attn_expand (the same
+ *   workspace size).
+ *
+ * bf16 contiguous caches with at most 64 query slots per 128-row tile (G >= 4
+ * for 128 rows) run one launch that rotates the queries as it loads them,
+ * stages the new nodes' rotated keys for its own tree tiles and has the work
+ * groups of row tile 0 write the new rows.  Other calls run the RoPE append
+ * (rotated queries into `out`) and then the attention launch on `out`.  `out`
+ * must not alias q, k_new, v_new or the cache.
+ */
+int tree_attn_verify_rope(const void* q, const void* k_new, const void* v_new, ta_kv kv,
+                          const int32_t* prefix_len, const int32_t* parent, const int32_t* n_nodes,
+                          int B, int n_max, int Hq, int Hkv, int d, int dtype, float scale,
+                          float base, void* out, float* lse, void* ws, size_t ws_bytes,
+                          const ta_attn_opts* opts, void* stream);
+int tree_attn_expand_rope(const void* q, const void* k_new, const void* v_new, ta_kv kv,
+                          const int32_t* prefix_len, const int32_t* parent, const int32_t* n_nodes,
+                          int B, int w, int n_max, int Hq, int Hkv, int d, int dtype, float scale,
+                          float base, void* out, float* lse, void* ws, size_t ws_bytes,
+                          const ta_attn_opts* opts, void* stream);
+
+/*
  * Greedy longest accepted path ([DL] how speculative decoding works and the
  * Acceptance Length entry: accept up to the first mismatch, then the
  * target's own token; AL in [1, 1 + D]).

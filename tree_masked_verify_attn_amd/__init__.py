@@ -7,6 +7,7 @@ entry points keep the C names:
 * ``tree_attn_verify``   -- tree-masked attention over every draft node
 * ``tree_attn_expand``   -- the same for the w newest leaves (non-square mask)
 * ``tree_attn_verify_noalloc`` -- verify with the library's fixed scratch (no allocation)
+* ``tree_attn_verify_rope`` / ``tree_attn_expand_rope`` -- the same with RoPE fused in
 * ``accept_greedy_path`` -- greedy longest accepted path, AL and bonus token
 * ``accept_sampling_path`` -- the same by speculative sampling (temperature > 0)
 * ``tree_cache_reroot``  -- evolving-tree-cache re-root with in-place KV moves
@@ -34,6 +35,8 @@ from ._lib import (  # noqa: F401
     tree_attn_expand,
     tree_attn_verify,
     tree_attn_verify_noalloc,
+    tree_attn_verify_rope,
+    tree_attn_expand_rope,
     tree_attn_workspace_bytes,
     tree_cache_reroot,
     tree_cache_reroot_draft,

@@ -32,6 +32,8 @@ EXPORTED_SYMBOLS = (
     "tree_attn_verify",
     "tree_attn_expand",
     "tree_attn_verify_noalloc",
+    "tree_attn_verify_rope",
+    "tree_attn_expand_rope",
     "accept_greedy_path",
     "accept_sampling_path",
     "accept_sampling_workspace_bytes",
@@ -103,6 +105,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.tree_attn_verify_noalloc.argtypes = attn + [c_int] * 6 + [
             f32, vp, vp, ctypes.POINTER(ta_attn_opts), vp]
         lib.tree_attn_verify_noalloc.restype = c_int
+        rope_head = [vp, vp, vp, ta_kv, vp, vp, vp]
+        lib.tree_attn_verify_rope.argtypes = rope_head + [c_int] * 6 + [
+            f32, f32, vp, vp, vp, c_size, ctypes.POINTER(ta_attn_opts), vp]
+        lib.tree_attn_verify_rope.restype = c_int
+        lib.tree_attn_expand_rope.argtypes = rope_head + [c_int] * 7 + [
+            f32, f32, vp, vp, vp, c_size, ctypes.POINTER(ta_attn_opts), vp]
+        lib.tree_attn_expand_rope.restype = c_int
         lib.accept_greedy_path.argtypes = [vp, c_int, vp, vp, vp, vp, c_int, c_int, c_int, vp, vp,
                                            vp, vp]
         lib.accept_greedy_path.restype = c_int
@@ -312,9 +321,10 @@ def _workspace_for(device, nbytes, stream=None):
 
 
 def _attention(fn_name, q, kv: KVCache, prefix_len, parent, n_nodes, scale, out, lse, workspace,
-               w, chunk_tokens, kernel, stream, with_lse):
+               w, chunk_tokens, kernel, stream, with_lse, rope=None):
     """Marshals one attention call; ``fn_name`` is "verify", "expand" or
-    "verify_noalloc" (no workspace: the library's fixed scratch array)."""
+    "verify_noalloc" (no workspace: the library's fixed scratch array);
+    ``rope`` = (k_new, v_new, base) selects the RoPE-fused entry points."""
     torch = _torch()
     lib = load_library()
     _need(q, "q", dtype=kv.dtype, ndim=4, device=kv.k.device)
@@ -366,6 +376,24 @@ def _attention(fn_name, q, kv: KVCache, prefix_len, parent, n_nodes, scale, out,
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     tail = (ctypes.c_float(scale), out.data_ptr(), _ptr(lse), _ptr(ws), ws_bytes,
             _opts(chunk_tokens, kernel), _stream(stream))
+    if rope is not None:
+        k_new, v_new, base = rope
+        for t, name in ((k_new, "k_new"), (v_new, "v_new")):
+            _need(t, name, dtype=q.dtype, ndim=4, device=dev)
+            if tuple(t.shape) != (B, n_q, kv.Hkv, d):
+                raise ValueError(f"{name} must be [B][n_q][Hkv][d] = {(B, n_q, kv.Hkv, d)}")
+        if out.data_ptr() in (q.data_ptr(), k_new.data_ptr(), v_new.data_ptr()):
+            raise ValueError("out must not alias q, k_new or v_new")
+        rtail = (ctypes.c_float(scale), ctypes.c_float(base)) + tail[1:]
+        head = (q.data_ptr(), k_new.data_ptr(), v_new.data_ptr()) + common[1:]
+        if fn_name == "verify":
+            if n_q != n_max:
+                raise ValueError("verify queries must be [B][n_max][Hq][d]")
+            st = lib.tree_attn_verify_rope(*head, B, n_max, Hq, kv.Hkv, d, dt, *rtail)
+        else:
+            st = lib.tree_attn_expand_rope(*head, B, w, n_max, Hq, kv.Hkv, d, dt, *rtail)
+        _check(st)
+        return out, lse
     if fn_name == "verify":
         if n_q != n_max:
             raise ValueError("verify queries must be [B][n_max][Hq][d]")
@@ -393,6 +421,28 @@ def tree_attn_verify_noalloc(q, kv: KVCache, prefix_len, parent, n_nodes, scale:
     Calls that overlap in time on one GPU race on that array."""
     return _attention("verify_noalloc", q, kv, prefix_len, parent, n_nodes, scale, out, lse,
                       None, 0, chunk_tokens, kernel, stream, with_lse)
+
+
+def tree_attn_verify_rope(q, k_new, v_new, kv: KVCache, prefix_len, parent, n_nodes, scale: float,
+                          base: float = 10000.0, out=None, lse=None, workspace=None,
+                          chunk_tokens: int = 0, kernel: int = 0, stream=None,
+                          with_lse: bool = True):
+    """Verification attention with RoPE fused in: rotates ``q`` and the new
+    nodes' keys ``k_new`` to their tree positions, writes keys and values
+    ``v_new`` to cache rows P + node, attends; returns ``(out, lse)``."""
+    return _attention("verify", q, kv, prefix_len, parent, n_nodes, scale, out, lse, workspace,
+                      0, chunk_tokens, kernel, stream, with_lse, rope=(k_new, v_new, float(base)))
+
+
+def tree_attn_expand_rope(q, k_new, v_new, kv: KVCache, prefix_len, parent, n_nodes, scale: float,
+                          base: float = 10000.0, out=None, lse=None, workspace=None,
+                          chunk_tokens: int = 0, kernel: int = 0, stream=None,
+                          with_lse: bool = True):
+    """Expansion attention for the ``w = q.shape[1]`` newest nodes with RoPE
+    fused in (their keys and values appended as by tree_rope_append)."""
+    return _attention("expand", q, kv, prefix_len, parent, n_nodes, scale, out, lse, workspace,
+                      int(q.shape[1]), chunk_tokens, kernel, stream, with_lse,
+                      rope=(k_new, v_new, float(base)))
 
 
 def tree_attn_expand(q, kv: KVCache, prefix_len, parent, n_nodes, scale: float, out=None,

@@ -197,7 +197,7 @@ int run_attention(const void* q, ta_kv kv, const int32_t* prefix_len, const int3
                   const int32_t* n_nodes, int B, int n_q, int n_max, int expand, int Hq, int Hkv,
                   int d, int dtype, float scale, void* out, float* lse, void* ws,
                   size_t ws_bytes, const ta_attn_opts* opts, void* stream,
-                  ScratchFn scratch) {
+                  ScratchFn scratch, const RopeArgs* rope) {
   int st = check_common(B, n_q, n_max, Hq, Hkv, d, dtype, kv.T_cap);
   if (st != TA_OK) return st;
   st = check_kv(kv);
@@ -225,6 +225,48 @@ int run_attention(const void* q, ta_kv kv, const int32_t* prefix_len, const int3
   }
   if (pl.ws_bytes > 0 && (ws == nullptr || ws_bytes < pl.ws_bytes || !aligned16(ws)))
     return TA_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  bool fused_rope = false;
+  if (rope != nullptr) {
+    if (rope->k_new == nullptr || rope->v_new == nullptr || out == q || !(rope->base > 0.f) ||
+        rope->base != rope->base || rope->base == INFINITY)
+      return TA_ERR_INVALID_ARG;
+    // Rotated on load by the streaming kernel when it serves the call; else the
+    // RoPE append writes the rotated queries into `out`, which the attention
+    // launch then reads as its queries (no kernel writes an output row that
+    // another work group still reads as a query).
+    fused_rope = pl.kernel == 3 && kv.block_table == nullptr &&
+                 ta::stream_rope_fits(d, pl.rows_per_tile, Hq / Hkv) &&
+                 aligned16(rope->k_new) && aligned16(rope->v_new);
+    if (!fused_rope) {
+      ta::RopeParams rp{};
+      rp.q_in = q;
+      rp.q_out = out;
+      rp.k_new = rope->k_new;
+      rp.v_new = rope->v_new;
+      rp.k = kv.k;
+      rp.v = kv.v;
+      rp.block_table = kv.block_table;
+      rp.block_size = kv.block_size;
+      rp.max_blocks = kv.max_blocks;
+      rp.num_blocks = kv.num_blocks;
+      rp.T_cap = kv.T_cap;
+      rp.prefix_len = prefix_len;
+      rp.parent = parent;
+      rp.n_nodes = n_nodes;
+      rp.B = B;
+      rp.n_q = n_q;
+      rp.n_max = n_max;
+      rp.Hq = Hq;
+      rp.Hkv = Hkv;
+      rp.d = d;
+      rp.expand = expand;
+      rp.base = rope->base;
+      const hipError_t e = ta::launch_rope_append(rp, dtype, s);
+      if (e != hipSuccess) return hip_status(e, "RoPE append launch");
+      q = out;
+    }
+  }
 
   AttnParams p{};
   p.q = q;
@@ -266,7 +308,12 @@ int run_attention(const void* q, ta_kv kv, const int32_t* prefix_len, const int3
     p.ws_o = reinterpret_cast<float*>(base);
     p.ws_ml = reinterpret_cast<float*>(base + parts * d * sizeof(float));
   }
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (fused_rope) {
+    p.rope = 1;
+    p.k_new = rope->k_new;
+    p.v_new = rope->v_new;
+    p.rope_base = rope->base;
+  }
   hipError_t e;
   const char* where;
   if (pl.kernel == 4) {
@@ -317,7 +364,7 @@ int tree_attn_verify(const void* q, ta_kv kv, const int32_t* prefix_len, const i
                      float scale, void* out, float* lse, void* ws, size_t ws_bytes,
                      const ta_attn_opts* opts, void* stream) {
   return ta::run_attention(q, kv, prefix_len, parent, n_nodes, B, n_max, n_max, 0, Hq, Hkv, d,
-                           dtype, scale, out, lse, ws, ws_bytes, opts, stream, nullptr);
+                           dtype, scale, out, lse, ws, ws_bytes, opts, stream, nullptr, nullptr);
 }
 
 int tree_attn_expand(const void* q, ta_kv kv, const int32_t* prefix_len, const int32_t* parent,
@@ -326,7 +373,28 @@ int tree_attn_expand(const void* q, ta_kv kv, const int32_t* prefix_len, const i
                      const ta_attn_opts* opts, void* stream) {
   if (w < 1 || w > n_max) return TA_ERR_INVALID_ARG;
   return ta::run_attention(q, kv, prefix_len, parent, n_nodes, B, w, n_max, 1, Hq, Hkv, d, dtype,
-                           scale, out, lse, ws, ws_bytes, opts, stream, nullptr);
+                           scale, out, lse, ws, ws_bytes, opts, stream, nullptr, nullptr);
+}
+
+int tree_attn_verify_rope(const void* q, const void* k_new, const void* v_new, ta_kv kv,
+                          const int32_t* prefix_len, const int32_t* parent, const int32_t* n_nodes,
+                          int B, int n_max, int Hq, int Hkv, int d, int dtype, float scale,
+                          float base, void* out, float* lse, void* ws, size_t ws_bytes,
+                          const ta_attn_opts* opts, void* stream) {
+  const ta::RopeArgs r{k_new, v_new, base};
+  return ta::run_attention(q, kv, prefix_len, parent, n_nodes, B, n_max, n_max, 0, Hq, Hkv, d,
+                           dtype, scale, out, lse, ws, ws_bytes, opts, stream, nullptr, &r);
+}
+
+int tree_attn_expand_rope(const void* q, const void* k_new, const void* v_new, ta_kv kv,
+                          const int32_t* prefix_len, const int32_t* parent, const int32_t* n_nodes,
+                          int B, int w, int n_max, int Hq, int Hkv, int d, int dtype, float scale,
+                          float base, void* out, float* lse, void* ws, size_t ws_bytes,
+                          const ta_attn_opts* opts, void* stream) {
+  if (w < 1 || w > n_max) return TA_ERR_INVALID_ARG;
+  const ta::RopeArgs r{k_new, v_new, base};
+  return ta::run_attention(q, kv, prefix_len, parent, n_nodes, B, w, n_max, 1, Hq, Hkv, d, dtype,
+                           scale, out, lse, ws, ws_bytes, opts, stream, nullptr, &r);
 }
 
 int accept_greedy_path(const void* logits, int logit_dtype, const int32_t* parent,

@@ -20,6 +20,18 @@
 //    ring loop issues no other vector-memory loads.
 //  * A split sequence leaves partial (max, sum, output) states in the
 //    workspace; the combine launch (attn_merge.hip) finishes it.
+//  * RoPE variant (kRope; SwiftSpec summary, Section 3.3: the masked
+//    attention takes the position embedding): the queries are rotated as
+//    they are loaded, to the positions P - 1 + depth of their nodes.  The ring
+//    then streams the prefix only; after it, the split's tree positions are
+//    staged in the ring's LDS, 32 at a time, the new nodes' keys rotated from
+//    k_new and their values from v_new (older nodes, when expanding, read
+//    from the cache), and attended as one more masked tile.  The work group
+//    of row tile 0 also writes the new nodes' rows to the cache (one writer
+//    per row); the others never read those rows from the cache.  At set-up
+//    only the first two stages are in flight: the other two slots hold the
+//    ancestor masks and the cos/sin table of the tile's query slots.
+#include "rope_common.h"
 #include "stream_common.h"
 
 namespace ta {
@@ -28,13 +40,16 @@ namespace {
 // S = 4: a 64 KiB ring, two work groups per compute unit.  (A three-stage
 // ring for three groups per CU does not fit: 128 query rows need the
 // registers of two.)
-template <int D, int NRG, int S>
+template <int D, int NRG, int S, bool kRope>
 __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) {
   using C = SCfg<D, NRG, S>;
   static_assert(S >= 2 && S <= 4, "ring depth");
+  static_assert(!kRope || S == 4, "the RoPE set-up uses two of four ring slots");
   __shared__ __attribute__((aligned(1024))) uint8_t sRing[C::LDS];
-  __shared__ int sBlk[kMaxSplitBlocks];
+  __shared__ int sBlk[kRope ? 1 : kMaxSplitBlocks];   // paged block ids (not with RoPE)
   __shared__ uint64_t sRowMask[C::RPT][kMaskWords];  // ancestor mask of each row's node
+  __shared__ int sDepth[kRope ? kMaxNodes : 1];      // RoPE: depth of every node
+  __shared__ double sInv[kRope ? D / 2 : 1];         // RoPE: base^(-2j/d)
 
   // grid = (sequence x KV head, split, row tile): consecutive work groups are
   // different (sequence, KV head) pairs, which the dispatcher deals round
@@ -71,9 +86,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
   }
   if (!__syncthreads_or(node >= 0)) return;
 
-  // ---- setup: ancestor masks (in the ring's space), paged block ids ------------
+  // With RoPE the ring streams the prefix part of the split; the tree part
+  // follows it (staged, not streamed).
+  const int t_ring_end = kRope ? min(t_end, sb.P) : t_end;
+  int vis_end = t_ring_end;  // the masked path's end of visible positions
   const bool has_tree = t_end > sb.P;
-  {
+
+  // ---- setup: ancestor masks (in the ring's space), paged block ids ------------
+  if constexpr (!kRope) {
     auto sAnc = reinterpret_cast<uint64_t(*)[kMaskWords]>(sRing);
     int* sJump = reinterpret_cast<int*>(sRing + kMaxNodes * kMaskWords * 8);
     if (has_tree) build_ancestor_masks(p.parent + static_cast<size_t>(b) * p.n_max, sb.n, sAnc, sJump);
@@ -117,14 +137,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
   const uint8_t* Kg = static_cast<const uint8_t*>(p.k);
   const uint8_t* Vg = static_cast<const uint8_t*>(p.v);
   const uint32_t ring_base = static_cast<uint32_t>(reinterpret_cast<size_t>((lds_u8*)sRing));
-  const int ntiles = (t_end - t_begin + kTile - 1) / kTile;
-  const int blk0 = p.block_table != nullptr ? t_begin / p.block_size : 0;
+  const int ntiles = max(0, (t_ring_end - t_begin + kTile - 1) / kTile);
+  const int blk0 = (!kRope && p.block_table != nullptr) ? t_begin / p.block_size : 0;
 
   // Byte offset of row `tok` (clamped into the split) of the K or V cache.
   auto row_bytes_off = [&](int tok) -> size_t {
-    tok = tok < t_end ? tok : t_end - 1;
+    tok = tok < t_ring_end ? tok : t_ring_end - 1;
     size_t row;
-    if (p.block_table != nullptr) {
+    if (!kRope && p.block_table != nullptr) {
       const int blk = sBlk[tok / p.block_size - blk0];
       row = (static_cast<size_t>(blk) * p.block_size + tok % p.block_size) * p.Hkv + hkv;
     } else {
@@ -135,7 +155,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
   // Per-lane DMA sources: lane (row r, physical chunk pc) of load q fetches
   // logical chunk pc ^ swz(r).  In the contiguous layout the byte offset of the
   // next stage to issue just advances by one tile of positions per stage.
-  const bool contiguous = p.block_table == nullptr;
+  const bool contiguous = kRope || p.block_table == nullptr;
   const size_t pos_stride = static_cast<size_t>(p.Hkv) * C::ROW;  // contiguous: bytes per position
   size_t dma_off[C::INST_PER_WAVE];
 #pragma unroll
@@ -149,7 +169,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
   auto issue_stage = [&](int j, int slot) {
     const int tb = t_begin + j * kTile;
     const uint32_t sbase = ring_base + slot * C::STAGE;
-    const bool fast = contiguous && tb + kTile <= t_end;
+    const bool fast = contiguous && tb + kTile <= t_ring_end;
 #pragma unroll
     for (int q = 0; q < C::INST_PER_WAVE; ++q) {
       const int r0 = (wave * C::INST_PER_WAVE + q) * C::ROWS_PER_INST;
@@ -174,7 +194,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
   float m_ref = -INFINITY;
   float l_sum = 0.f;
   const float cs = p.scale_log2;
-  const int lim = min(sb.P, t_end);
+  const int lim = min(sb.P, t_ring_end);
 
   // S^T = K . Q^T for the tile in ring `slot` (M = 32 positions, N = 32 rows,
   // K = d).  The MFMAs run while the previous tile's softmax uses the VALU.
@@ -205,21 +225,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
     v_base_m = L - 64 * x;
   }
   // Mask (tiles that reach the tree cache or the split's end), online softmax
-  // and O^T += V^T . P^T for tile j held in ring `slot`.  Lane l holds
-  // positions tb + 8*(r/4) + 4*lhi + r%4 of row l32.
-  auto softmax_pv = [&](f32x16 Sc, int j, int slot, auto masked_tag) {
+  // and O^T += V^T . P^T for the tile of positions tb.. held in ring `slot`.
+  // Lane l holds positions tb + 8*(r/4) + 4*lhi + r%4 of row l32.
+  auto softmax_pv = [&](f32x16 Sc, int tb, int slot, auto masked_tag) {
     constexpr bool kMasked = decltype(masked_tag)::value;
-    const int tb = t_begin + j * kTile;
     const uint8_t* sV = sRing + slot * C::STAGE + C::HALF;
     if constexpr (kMasked) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int t = tb + 8 * (r >> 2) + 4 * lhi + (r & 3);
         const int jj = t - sb.P;  // tree column (negative: prefix)
-        const bool tree_col = jj >= 0 && t < t_end;  // then jj < n <= 256
+        const bool tree_col = jj >= 0 && t < vis_end;  // then jj < n <= 256
         const uint64_t word = tree_col ? sRowMask[row_in_tile][jj >> 6] : 0ull;
         const bool in_tree = ((word >> (jj & 63)) & 1ull) != 0ull;
-        const bool vis = t < t_end && (jj < 0 || in_tree);
+        const bool vis = t < vis_end && (jj < 0 || in_tree);
         if (!vis) Sc[r] = -INFINITY;
       }
     }
@@ -280,10 +299,82 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
   };
 
   // Prologue: stages 0 .. S-2 and the queries in flight, tile 0's scores started.
-  for (int j = 0; j < S - 1 && j < ntiles; ++j) issue_stage(j, j);
-  load_q();
-  arrive(0, 0);
-  f32x16 s_cur = rg >= 0 ? qk(0) : f32x16{};
+  if constexpr (!kRope) {
+    for (int j = 0; j < S - 1 && j < ntiles; ++j) issue_stage(j, j);
+    load_q();
+  } else {
+    // Stages 0 .. S-3 go out first; ring slots S-2 and S-1 hold the set-up.
+    for (int j = 0; j < S - 2 && j < ntiles; ++j) issue_stage(j, j);
+    uint8_t* setup = sRing + (S - 2) * C::STAGE;
+    auto sAnc = reinterpret_cast<uint64_t(*)[kMaskWords]>(setup);
+    int* sJump = reinterpret_cast<int*>(setup + kMaxNodes * kMaskWords * 8);
+    if (tid < D / 2) sInv[tid] = rope_inv_freq(p.rope_base, tid, D);
+    build_ancestor_masks(p.parent + static_cast<size_t>(b) * p.n_max, sb.n, sAnc, sJump);
+    if (has_tree && rg >= 0 && lhi == 0) {
+#pragma unroll
+      for (int w = 0; w < kMaskWords; ++w) sRowMask[row_in_tile][w] = node >= 0 ? sAnc[node][w] : 0ull;
+    }
+    for (int i = tid; i < sb.n; i += kThreads) {
+      int dep = 0;
+#pragma unroll
+      for (int w = 0; w < kMaskWords; ++w) dep += __popcll(sAnc[i][w]);
+      sDepth[i] = dep;  // the node and its ancestors: its depth below the root
+    }
+    __syncthreads();
+    // cos/sin of the tile's query slots (they overwrite the masks)
+    const int slot_lo = rtile * C::RPT / p.G;
+    const int slot_hi = min(p.n_q, ((rtile + 1) * C::RPT - 1) / p.G + 1);
+    float2* sTab = reinterpret_cast<float2*>(setup);
+    for (int e = tid; e < (slot_hi - slot_lo) * (D / 2); e += kThreads) {
+      const int sl = slot_lo + e / (D / 2), j = e % (D / 2);
+      const int nd = p.expand ? sb.n - p.n_q + sl : sl;
+      float c = 1.f, sn = 0.f;
+      if (nd >= 0 && nd < sb.n) rope_cos_sin(sb.P - 1 + sDepth[nd], sInv[j], c, sn);
+      sTab[e] = float2{c, sn};
+    }
+    __syncthreads();
+    // queries: each lane holds chunks 2ks + lhi; chunk c pairs with c + D/16
+    // (channels j and j + d/2), which is qreg[ks + KS/2] of the same lane
+    {
+      const uint16_t* Q = static_cast<const uint16_t*>(p.q);
+      const size_t qrow = ((static_cast<size_t>(b) * p.n_q + slot) * p.Hq + hkv * p.G + g) * D;
+      u32x4 raw[C::KS];
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        raw[ks] = u32x4{0u, 0u, 0u, 0u};
+        if (node >= 0) raw[ks] = *reinterpret_cast<const u32x4*>(Q + qrow + (2 * ks + lhi) * 8);
+      }
+      const float2* tab = sTab + (slot - slot_lo) * (D / 2);
+#pragma unroll
+      for (int ks = 0; ks < C::KS / 2; ++ks) {
+        const uint32_t w0[4] = {raw[ks].x, raw[ks].y, raw[ks].z, raw[ks].w};
+        const uint32_t w1[4] = {raw[ks + C::KS / 2].x, raw[ks + C::KS / 2].y,
+                                raw[ks + C::KS / 2].z, raw[ks + C::KS / 2].w};
+        uint32_t o0[4], o1[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          float y[2][2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int j = (2 * ks + lhi) * 8 + 2 * h + e;
+            const float x0 = __uint_as_float(e ? (w0[h] & 0xffff0000u) : (w0[h] << 16));
+            const float x1 = __uint_as_float(e ? (w1[h] & 0xffff0000u) : (w1[h] << 16));
+            const float2 cs2 = node >= 0 ? tab[j] : float2{1.f, 0.f};
+            rope_rotate(x0, x1, cs2.x, cs2.y, y[0][e], y[1][e]);
+          }
+          o0[h] = f32_to_bf16_bits(y[0][0]) | (static_cast<uint32_t>(f32_to_bf16_bits(y[0][1])) << 16);
+          o1[h] = f32_to_bf16_bits(y[1][0]) | (static_cast<uint32_t>(f32_to_bf16_bits(y[1][1])) << 16);
+        }
+        qreg[ks] = __builtin_bit_cast(bf16x8, u32x4{o0[0], o0[1], o0[2], o0[3]});
+        qreg[ks + C::KS / 2] = __builtin_bit_cast(bf16x8, u32x4{o1[0], o1[1], o1[2], o1[3]});
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the query loads (and the first stages)
+    }
+    __syncthreads();  // the table is done with: slot S-2 takes its stage
+    if (S - 2 < ntiles) issue_stage(S - 2, S - 2);
+  }
+  if (ntiles > 0) arrive(0, 0);
+  f32x16 s_cur = (rg >= 0 && ntiles > 0) ? qk(0) : f32x16{};
   // Iteration j: tile j+1 arrives and its scores start on the matrix cores,
   // then tile j's softmax and P.V run.  Tiles below lim = min(P, t_end) need no
   // mask; the dense part is unrolled by the ring depth so that every slot
@@ -296,7 +387,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
       arrive(j + u + 1, (u + 1) % S);
       if (rg >= 0) {
         const f32x16 s_next = qk((u + 1) % S);
-        softmax_pv(s_cur, j + u, u, std::false_type{});
+        softmax_pv(s_cur, t_begin + (j + u) * kTile, u, std::false_type{});
         s_cur = s_next;
       }
     }
@@ -314,9 +405,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
           f32x16 s_next = {};
           if (more) s_next = qk((u + 1) % S);
           if (jj < n_clean)
-            softmax_pv(s_cur, jj, u, std::false_type{});
+            softmax_pv(s_cur, t_begin + jj * kTile, u, std::false_type{});
           else
-            softmax_pv(s_cur, jj, u, std::true_type{});
+            softmax_pv(s_cur, t_begin + jj * kTile, u, std::true_type{});
           s_cur = s_next;
         }
       }
@@ -324,6 +415,91 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
   }
   wait_vmcnt<0>();
   __syncthreads();
+
+  // ---- RoPE: the split's tree positions, 32 at a time, staged in slot 0 ----
+  if constexpr (kRope) {
+    const int first_new = p.expand ? sb.n - p.n_q : 0;  // new nodes: [first_new, n)
+    const uint16_t* Kn = static_cast<const uint16_t*>(p.k_new);
+    const uint16_t* Vn = static_cast<const uint16_t*>(p.v_new);
+    uint16_t* Kc = static_cast<uint16_t*>(const_cast<void*>(p.k));
+    uint16_t* Vc = static_cast<uint16_t*>(const_cast<void*>(p.v));
+    const bool writer = rtile == 0;
+    float2* sTab = reinterpret_cast<float2*>(sRing + 2 * C::STAGE);  // [32][D/2]
+    uint8_t* sK = sRing;
+    uint8_t* sV = sRing + C::HALF;
+    vis_end = t_end;
+    for (int c0 = max(sb.P, t_begin); c0 < t_end; c0 += kTile) {
+      for (int e = tid; e < kTile * (D / 2); e += kThreads) {
+        const int r = e / (D / 2), j = e % (D / 2);
+        const int nd = c0 + r - sb.P;
+        float c = 1.f, sn = 0.f;
+        if (c0 + r < t_end && nd >= first_new) rope_cos_sin(sb.P - 1 + sDepth[nd], sInv[j], c, sn);
+        sTab[e] = float2{c, sn};
+      }
+      __syncthreads();
+      // keys: (row, chunk pair) items; values: (row, chunk) items
+      for (int e = tid; e < kTile * (C::CH / 2); e += kThreads) {
+        const int r = e / (C::CH / 2), cp = e % (C::CH / 2);
+        const int t = c0 + r, nd = t - sb.P;
+        u32x4 a = {0u, 0u, 0u, 0u}, z = {0u, 0u, 0u, 0u};
+        if (t < t_end) {
+          const size_t crow = ((static_cast<size_t>(b) * p.T_cap + t) * p.Hkv + hkv) * D;
+          if (nd >= first_new) {
+            const size_t nrow =
+                ((static_cast<size_t>(b) * p.n_q + (nd - first_new)) * p.Hkv + hkv) * D;
+            const u32x4 x = *reinterpret_cast<const u32x4*>(Kn + nrow + cp * 8);
+            const u32x4 y = *reinterpret_cast<const u32x4*>(Kn + nrow + (cp + C::CH / 2) * 8);
+            const uint32_t wx[4] = {x.x, x.y, x.z, x.w}, wy[4] = {y.x, y.y, y.z, y.w};
+            uint32_t ox[4], oy[4];
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+              float r0[2], r1[2];
+#pragma unroll
+              for (int q = 0; q < 2; ++q) {
+                const float x0 = __uint_as_float(q ? (wx[h] & 0xffff0000u) : (wx[h] << 16));
+                const float x1 = __uint_as_float(q ? (wy[h] & 0xffff0000u) : (wy[h] << 16));
+                const float2 cs2 = sTab[r * (D / 2) + cp * 8 + 2 * h + q];
+                rope_rotate(x0, x1, cs2.x, cs2.y, r0[q], r1[q]);
+              }
+              ox[h] = f32_to_bf16_bits(r0[0]) | (static_cast<uint32_t>(f32_to_bf16_bits(r0[1])) << 16);
+              oy[h] = f32_to_bf16_bits(r1[0]) | (static_cast<uint32_t>(f32_to_bf16_bits(r1[1])) << 16);
+            }
+            a = u32x4{ox[0], ox[1], ox[2], ox[3]};
+            z = u32x4{oy[0], oy[1], oy[2], oy[3]};
+            if (writer) {
+              *reinterpret_cast<u32x4*>(Kc + crow + cp * 8) = a;
+              *reinterpret_cast<u32x4*>(Kc + crow + (cp + C::CH / 2) * 8) = z;
+            }
+          } else {  // an older node (expanding): already rotated in the cache
+            a = *reinterpret_cast<const u32x4*>(Kc + crow + cp * 8);
+            z = *reinterpret_cast<const u32x4*>(Kc + crow + (cp + C::CH / 2) * 8);
+          }
+        }
+        *reinterpret_cast<u32x4*>(sK + lds_off<D>(r, cp)) = a;
+        *reinterpret_cast<u32x4*>(sK + lds_off<D>(r, cp + C::CH / 2)) = z;
+      }
+      for (int e = tid; e < kTile * C::CH; e += kThreads) {
+        const int r = e / C::CH, c = e % C::CH;
+        const int t = c0 + r, nd = t - sb.P;
+        u32x4 a = {0u, 0u, 0u, 0u};
+        if (t < t_end) {
+          const size_t crow = ((static_cast<size_t>(b) * p.T_cap + t) * p.Hkv + hkv) * D;
+          if (nd >= first_new) {
+            const size_t nrow =
+                ((static_cast<size_t>(b) * p.n_q + (nd - first_new)) * p.Hkv + hkv) * D;
+            a = *reinterpret_cast<const u32x4*>(Vn + nrow + c * 8);
+            if (writer) *reinterpret_cast<u32x4*>(Vc + crow + c * 8) = a;
+          } else {
+            a = *reinterpret_cast<const u32x4*>(Vc + crow + c * 8);
+          }
+        }
+        *reinterpret_cast<u32x4*>(sV + lds_off<D>(r, c)) = a;
+      }
+      __syncthreads();
+      if (rg >= 0) softmax_pv(qk(0), c0, 0, std::true_type{});
+      __syncthreads();  // before the next group of positions overwrites slot 0
+    }
+  }
 
   uint16_t* Out = static_cast<uint16_t*>(p.out);
   const size_t orow = ((static_cast<size_t>(b) * p.n_q + slot) * p.Hq + hkv * p.G + g) * D;
@@ -368,24 +544,39 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
   // the combine launch (attn_merge.hip) finishes split sequences
 }
 
-template <int D, int S>
+template <int D, int S, bool R>
 hipError_t launch_ds(const AttnParams& p, hipStream_t s) {
   const dim3 grid(p.B * p.Hkv, p.n_split, p.n_row_tiles);
   const dim3 block(kThreads);
   switch (p.rows_per_tile / 32) {
-    case 1: return launch(attn_stream_kernel<D, 1, S>, grid, block, s, p);
-    case 2: return launch(attn_stream_kernel<D, 2, S>, grid, block, s, p);
-    case 3: return launch(attn_stream_kernel<D, 3, S>, grid, block, s, p);
-    case 4: return launch(attn_stream_kernel<D, 4, S>, grid, block, s, p);
+    case 1: return launch(attn_stream_kernel<D, 1, S, R>, grid, block, s, p);
+    case 2: return launch(attn_stream_kernel<D, 2, S, R>, grid, block, s, p);
+    case 3: return launch(attn_stream_kernel<D, 3, S, R>, grid, block, s, p);
+    case 4: return launch(attn_stream_kernel<D, 4, S, R>, grid, block, s, p);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
+bool stream_rope_fits(int d, int rows_per_tile, int G) {
+  // cos/sin (8 bytes) of d/2 pairs for every query slot a row tile touches,
+  // in two 32-position ring stages of d-wide bf16 K and V rows (256 d bytes);
+  // the tree phase's table of 32 positions needs 128 d bytes of the same
+  const long long slots = rows_per_tile / G + 1;
+  return slots * (d / 2) * 8 <= 2LL * 4 * 32 * d && (d == 64 || d == 128);
+}
+
 hipError_t launch_attn_stream(const AttnParams& p, hipStream_t s) {
-  if (p.d == 128) return launch_ds<128, 4>(p, s);
-  if (p.d == 64) return launch_ds<64, 4>(p, s);
+  if (p.rope) {
+    if (p.block_table != nullptr || !stream_rope_fits(p.d, p.rows_per_tile, p.G))
+      return hipErrorInvalidValue;
+    if (p.d == 128) return launch_ds<128, 4, true>(p, s);
+    if (p.d == 64) return launch_ds<64, 4, true>(p, s);
+    return hipErrorInvalidValue;
+  }
+  if (p.d == 128) return launch_ds<128, 4, false>(p, s);
+  if (p.d == 64) return launch_ds<64, 4, false>(p, s);
   return hipErrorInvalidValue;
 }
 

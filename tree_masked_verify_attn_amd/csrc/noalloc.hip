@@ -64,5 +64,6 @@ extern "C" int tree_attn_verify_noalloc(const void* q, ta_kv kv, const int32_t* 
                                         void* out, float* lse, const ta_attn_opts* opts,
                                         void* stream) {
   return ta::run_attention(q, kv, prefix_len, parent, n_nodes, B, n_max, n_max, 0, Hq, Hkv, d,
-                           dtype, scale, out, lse, nullptr, 0, opts, stream, device_scratch);
+                           dtype, scale, out, lse, nullptr, 0, opts, stream, device_scratch,
+                           nullptr);
 }

@@ -15,11 +15,12 @@
 // One work group per (query slot, sequence): the node's depth from a walk up
 // the parent links in LDS, the angles reduced modulo 2 pi in double precision
 // (positions reach tens of thousands, where a float product would be off by
-// ~1e-3 rad), cos/sin tabulated in LDS, then every query head, key head and
+// ~1e-3 rad; rope_common.h), cos/sin tabulated in LDS, then every query head, key head and
 // value head of the slot.  With 16-byte aligned rows a thread moves whole
 // 16-byte vectors (a vector of channels j.. and its partner j + d/2 ..), and
 // its first four items are loaded before the depth walk and the angles, so
 // that those latencies overlap.
+#include "rope_common.h"
 #include "ta_device.h"
 
 namespace ta {
@@ -67,13 +68,7 @@ __global__ __launch_bounds__(kThreads) void rope_append_kernel(RopeParams p) {
   __syncthreads();
   const int pos = sb.P - 1 + sDepth;
   const int half = p.d / 2;
-  if (tid < half) {
-    const double inv = pow(static_cast<double>(p.base), -2.0 * tid / p.d);
-    const double two_pi = 6.283185307179586476925286766559;
-    double a = fmod(static_cast<double>(pos) * inv, two_pi);
-    sCos[tid] = static_cast<float>(cos(a));
-    sSin[tid] = static_cast<float>(sin(a));
-  }
+  if (tid < half) rope_cos_sin(pos, rope_inv_freq(p.base, tid, p.d), sCos[tid], sSin[tid]);
   __syncthreads();
 
   const T* q = static_cast<const T*>(p.q_in);
@@ -84,8 +79,10 @@ __global__ __launch_bounds__(kThreads) void rope_append_kernel(RopeParams p) {
     const int h = e / half, j = e % half;
     const size_t o = qrow + static_cast<size_t>(h) * p.d + j;
     const float x0 = ld<T>(q, o), x1 = ld<T>(q, o + half);
-    st<T>(qo, o, x0 * sCos[j] - x1 * sSin[j]);
-    st<T>(qo, o + half, x1 * sCos[j] + x0 * sSin[j]);
+    float y0, y1;
+    rope_rotate(x0, x1, sCos[j], sSin[j], y0, y1);
+    st<T>(qo, o, y0);
+    st<T>(qo, o + half, y1);
   }
   // keys (rotated) and values (copied) into cache row P + node
   const T* kn = static_cast<const T*>(p.k_new);
@@ -99,8 +96,10 @@ __global__ __launch_bounds__(kThreads) void rope_append_kernel(RopeParams p) {
     const size_t c = kv_offset(p.block_table, p.block_size, p.max_blocks, p.num_blocks, p.T_cap,
                                p.Hkv, p.d, b, sb.P + node, h) + j;
     const float x0 = ld<T>(kn, i), x1 = ld<T>(kn, i + half);
-    st<T>(K, c, x0 * sCos[j] - x1 * sSin[j]);
-    st<T>(K, c + half, x1 * sCos[j] + x0 * sSin[j]);
+    float y0, y1;
+    rope_rotate(x0, x1, sCos[j], sSin[j], y0, y1);
+    st<T>(K, c, y0);
+    st<T>(K, c + half, y1);
     Vc[c] = vn[i];
     Vc[c + half] = vn[i + half];
   }
@@ -202,11 +201,7 @@ __global__ __launch_bounds__(kThreads) void rope_append_vec_kernel(RopeParams p)
     VT::unpack(w1, x1);
     const int j0 = (it < nQ ? it : it - nQ) % hv * kV;
 #pragma unroll
-    for (int e = 0; e < kV; ++e) {
-      const float c = sCos[j0 + e], sn = sSin[j0 + e];
-      y0[e] = x0[e] * c - x1[e] * sn;
-      y1[e] = x1[e] * c + x0[e] * sn;
-    }
+    for (int e = 0; e < kV; ++e) rope_rotate(x0[e], x1[e], sCos[j0 + e], sSin[j0 + e], y0[e], y1[e]);
     T* dst;
     size_t o;
     if (it < nQ) {
@@ -247,13 +242,7 @@ __global__ __launch_bounds__(kThreads) void rope_append_vec_kernel(RopeParams p)
   }
   __syncthreads();
   const int pos = sb.P - 1 + sDepth;
-  if (tid < half) {
-    const double inv = pow(static_cast<double>(p.base), -2.0 * tid / p.d);
-    const double two_pi = 6.283185307179586476925286766559;
-    double a = fmod(static_cast<double>(pos) * inv, two_pi);
-    sCos[tid] = static_cast<float>(cos(a));
-    sSin[tid] = static_cast<float>(sin(a));
-  }
+  if (tid < half) rope_cos_sin(pos, rope_inv_freq(p.base, tid, p.d), sCos[tid], sSin[tid]);
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < kEarly; ++i) {

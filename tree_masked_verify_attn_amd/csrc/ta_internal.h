@@ -64,6 +64,14 @@ struct AttnParams {
   // hold 2G slots of rows_per_tile rows, ws_seq the stream start of every
   // sequence and the stream's length (B + 1 entries)
   int32_t* ws_seq;
+  // RoPE on load (streaming kernel only, contiguous caches): q holds the
+  // un-rotated queries, k_new / v_new [B][n_q][Hkv][d] the new nodes' keys
+  // (un-rotated) and values, which the kernel rotates, attends to and writes
+  // to cache rows P + node (the work groups of row tile 0).
+  const void* k_new;
+  const void* v_new;
+  float rope_base;
+  int32_t rope;
 };
 
 // One attention call (tree_attn_verify / tree_attn_expand): validation,
@@ -71,10 +79,18 @@ struct AttnParams {
 // ignored and scratch(bytes the plan needs, stream, &ws) supplies the buffer
 // once the plan is known (only when the plan needs one).
 typedef int (*ScratchFn)(size_t need, void* stream, void** ws);
+// RoPE at tree positions as part of the call (tree_attn_*_rope): the new
+// nodes' keys and values [B][n_q][Hkv][d] and the base.
+struct RopeArgs {
+  const void* k_new;
+  const void* v_new;
+  float base;
+};
 int run_attention(const void* q, ta_kv kv, const int32_t* prefix_len, const int32_t* parent,
                   const int32_t* n_nodes, int B, int n_q, int n_max, int expand, int Hq, int Hkv,
                   int d, int dtype, float scale, void* out, float* lse, void* ws,
-                  size_t ws_bytes, const ta_attn_opts* opts, void* stream, ScratchFn scratch);
+                  size_t ws_bytes, const ta_attn_opts* opts, void* stream, ScratchFn scratch,
+                  const RopeArgs* rope);
 
 // Workspace layout: the partial outputs, then the (max, sum) pairs.  Returns
 // the bytes needed for a plan (0 when there is a single split).
@@ -86,6 +102,9 @@ hipError_t launch_attn_merge(const AttnParams& p, int dtype, hipStream_t s);
 hipError_t launch_attn_mfma(const AttnParams& p, hipStream_t s);
 // Streaming MFMA variant: a ring of four 32-position LDS stages.
 hipError_t launch_attn_stream(const AttnParams& p, hipStream_t s);
+// Whether the streaming kernel can rotate on load for these sizes (its
+// cos/sin table of one row tile's query slots fits two ring stages).
+bool stream_rope_fits(int d, int rows_per_tile, int G);
 constexpr int kStreamMaxSplitBlocks = 512;  // paged: block ids of one split held in LDS
 // Units kernel: every (sequence, row tile, KV head) job's tiles laid end to end,
 // G equal ranges of them, one per work group; then a combine launch.
