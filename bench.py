@@ -4,7 +4,7 @@ Default workload, ``chain_verify``: batch 16, Hq=64, Hkv=8, d=128, bf16,
 prefix 32768 per sequence, D = 15 chain drafts -> 128 query rows per KV head.
 One step = one pass of the whole path over one batch:
 
-    tree_attn_verify -> accept_greedy_path -> tree_cache_reroot
+    tree_attn_verify -> tree_accept_reroot (greedy accept + re-root, 2 launches)
 
 followed by restoring the three tiny per-sequence arrays the re-root rewrote
 (prefix_len, parent, n_nodes: one small elementwise kernel), so that every
@@ -209,21 +209,33 @@ class _VerifyBatch:
         self.bytes = attn_bytes(c.prefix_len, c.n_nodes, c.n_nodes, c.Hq, c.Hkv, c.d)
 
     def phase(self, j, ws, opts, kv=None, q=None, logits=None):
-        """Phase j of one step: 0 verify attention, 1 accept, 2 re-root + restore."""
+        """Phase j of one step: 0 verify attention, 1 greedy accept + re-root
+        (tree_accept_reroot) + restore."""
         ta = self.ta
         kv = self.kv if kv is None else kv
         if j == 0:
             ta.tree_attn_verify(self.q if q is None else q, kv, self.P, self.par, self.n,
                                 self.c.scale, out=self.out, lse=self.lse, workspace=ws, **opts)
-        elif j == 1:
-            ta.accept_greedy_path(self.logits if logits is None else logits, self.par, self.tok,
-                                  self.n, self.root_tok, self.path, self.plen, self.bonus)
         else:
-            ta.tree_cache_reroot([kv], self.P, self.par, self.n, self.path, self.plen, self.keep)
-            # an elementwise kernel, not a device copy, so that it graph-captures
-            # as a kernel node
-            torch = self.torch
-            torch.add(self.meta0, 0, out=self.meta)
+            ta.tree_accept_reroot(self.logits if logits is None else logits, self.tok,
+                                  self.root_tok, [kv], self.P, self.par, self.n, self.keep,
+                                  self.path, self.plen, self.bonus, workspace=ws)
+            self.restore()
+
+    def restore(self):
+        # an elementwise kernel, not a device copy, so that it graph-captures
+        # as a kernel node
+        self.torch.add(self.meta0, 0, out=self.meta)
+
+    def two_calls(self, kv=None, logits=None):
+        """The same accept + re-root as accept_greedy_path then
+        tree_cache_reroot (four launches), timed beside the step."""
+        ta = self.ta
+        kv = self.kv if kv is None else kv
+        ta.accept_greedy_path(self.logits if logits is None else logits, self.par, self.tok,
+                              self.n, self.root_tok, self.path, self.plen, self.bonus)
+        ta.tree_cache_reroot([kv], self.P, self.par, self.n, self.path, self.plen, self.keep)
+        self.restore()
 
 
 class _Workload:
@@ -241,7 +253,7 @@ class _Workload:
 
 
 class ChainVerify(_Workload):
-    phases = ("verify", "accept", "reroot")
+    phases = ("verify", "accept_reroot")
 
     def __init__(self, ta, up):
         from gen import config2_chain
@@ -253,7 +265,7 @@ class ChainVerify(_Workload):
         self.config = {"workload": "chain_verify", "batch": c.B, "Hq": c.Hq, "Hkv": c.Hkv,
                        "head_dim": c.d, "prefix": int(c.prefix_len[0]), "D": c.n_max - 1,
                        "rows_per_kv_head": c.G * c.n_max, "vocab": c.vocab,
-                       "step": "verify + accept + re-root (+ restore of 3 tiny arrays)"}
+                       "step": "verify + accept/re-root (+ restore of 3 tiny arrays)"}
 
     def phase(self, i, j, ws, opts):
         self.batch.phase(j, ws, opts)
@@ -304,7 +316,8 @@ class ChainVerify(_Workload):
             # staged and written by the attention kernel)
             bt.ta.tree_attn_verify_rope(bt.q, k_new, v_new, bt.kv, bt.P, bt.par, bt.n, c.scale,
                                         out=out_r, lse=lse_r, workspace=ws, **opts)
-        return {"rope_append": rope, "accept_sampling": sampling, "verify_rope": verify_rope}
+        return {"rope_append": rope, "accept_sampling": sampling, "verify_rope": verify_rope,
+                "accept_then_reroot": lambda i, ws, opts: bt.two_calls()}
 
     def attn_bytes(self, i):
         return self.batch.bytes
@@ -318,7 +331,7 @@ class ChainVerify(_Workload):
 
 
 class PagedAlternating(_Workload):
-    phases = ("verify", "accept", "reroot")
+    phases = ("verify", "accept_reroot")
 
     def __init__(self, ta, up):
         from gen import config5_paged
@@ -334,11 +347,16 @@ class PagedAlternating(_Workload):
         self.config = {"workload": "paged_alternating", "batch": m, "resident_requests": c.B,
                        "Hq": c.Hq, "Hkv": c.Hkv, "head_dim": c.d, "prefix": "U[512,8192]",
                        "block_size": c.block_size, "k": c.n_max - 1, "vocab": c.vocab,
-                       "step": "verify + accept + re-root of batch (step mod 2)"}
+                       "step": "verify + accept/re-root of batch (step mod 2)"}
 
     def phase(self, i, j, ws, opts):
         self.ran.add(i % 2)
         self.batches[i % 2].phase(j, ws, opts)
+
+    def extras(self):
+        """accept_greedy_path then tree_cache_reroot (four launches) on the
+        step's batch, timed beside the step."""
+        return {"accept_then_reroot": lambda i, ws, opts: self.batches[i % 2].two_calls()}
 
     def attn_bytes(self, i):
         return self.batches[i % 2].bytes
@@ -358,7 +376,7 @@ class PagedAlternating(_Workload):
 class TreeVerifyL70b(_Workload):
     """Rotates over COPIES sets of (K, V, Q, logits) so that nothing a step
     reads is left in the Infinity Cache by the previous steps."""
-    phases = ("verify", "accept", "reroot")
+    phases = ("verify", "accept_reroot")
     COPIES = 16
 
     def __init__(self, ta, up):
@@ -373,11 +391,19 @@ class TreeVerifyL70b(_Workload):
         self.config = {"workload": "tree_verify_l70b", "batch": c.B, "Hq": c.Hq, "Hkv": c.Hkv,
                        "head_dim": c.d, "prefix": int(c.prefix_len[0]), "tree_nodes": c.n_max,
                        "vocab": c.vocab, "kv_copies": self.COPIES,
-                       "step": "verify + accept + re-root (+ restore of 3 tiny arrays)"}
+                       "step": "verify + accept/re-root (+ restore of 3 tiny arrays)"}
 
     def phase(self, i, j, ws, opts):
         c = i % self.COPIES
         self.batch.phase(j, ws, opts, kv=self.kvs[c], q=self.qs[c], logits=self.lgs[c])
+
+    def extras(self):
+        """accept_greedy_path then tree_cache_reroot (four launches), timed
+        beside the step."""
+        def two(i, ws, opts):
+            c = i % self.COPIES
+            self.batch.two_calls(kv=self.kvs[c], logits=self.lgs[c])
+        return {"accept_then_reroot": two}
 
     def attn_bytes(self, i):
         return self.batch.bytes

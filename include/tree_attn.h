@@ -252,6 +252,37 @@ int tree_cache_reroot_draft(const ta_kv* kv_layers, int n_layers, int32_t* prefi
                             void* stream);
 
 /*
+ * accept_greedy_path followed by tree_cache_reroot on the path it finds, in
+ * two launches instead of four: the same outputs and the same final caches
+ * and metadata, bit for bit ([DL] Acceptance Length entry; [SS] Section 3.2,
+ * Figure 4).  The target side's verify step ends with it.
+ *
+ *   logits, logit_dtype, tok, root_tok, V: as for accept_greedy_path
+ *   kv_layers, n_layers, prefix_len, parent, n_nodes, keep_subtree, Hkv, d,
+ *   dtype: as for tree_cache_reroot (prefix_len, parent, n_nodes in/out)
+ *   path, path_len, bonus: outputs as for accept_greedy_path (the path
+ *            before the re-root renumbers the nodes)
+ *   ws       device workspace of tree_accept_reroot_workspace_bytes(B, n_max)
+ *            bytes, 16-byte aligned: the argmax per node and a copy of
+ *            prefix_len, parent and n_nodes.  Its contents need no
+ *            initialisation and are meaningless between calls.  Calls that
+ *            overlap in time must not share a workspace.
+ *
+ * The first launch takes every node's argmax and copies the metadata.  In
+ * the second (one more per 32 layers past the first 32), every work group of
+ * the re-root move finds the accepted path itself from the copy, and one
+ * group per sequence writes the path and the new metadata.  Errors as for
+ * the two calls, plus TA_ERR_WORKSPACE.
+ */
+size_t tree_accept_reroot_workspace_bytes(int B, int n_max);
+int tree_accept_reroot(const void* logits, int logit_dtype, const int32_t* tok,
+                       const int32_t* root_tok, const ta_kv* kv_layers, int n_layers,
+                       int32_t* prefix_len, int32_t* parent, int32_t* n_nodes,
+                       const uint8_t* keep_subtree, int B, int n_max, int V, int Hkv, int d,
+                       int dtype, int32_t* path, int32_t* path_len, int32_t* bonus, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/*
  * Tree verification by speculative sampling, temperature > 0 ([MD] the
  * PEARL walkthrough: a rejected draft token is replaced by a draw from
  * norm(max(0, p - q)); [MD] experimental setup: sampling at temperature

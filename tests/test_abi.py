@@ -241,3 +241,44 @@ def test_accept_sampling_host_side_validation():
     assert call(ws=None) == _lib.TA_ERR_WORKSPACE
     assert call(ws_bytes=ws_need - 1) == _lib.TA_ERR_WORKSPACE
     assert call(ws=P + 8) == _lib.TA_ERR_WORKSPACE
+
+
+def _accept_reroot(lib, **kw):
+    a = dict(lg=0x1000, ldt=ta.TA_F32, tok=0x2000, rt=0x3000, arr=(_lib.ta_kv * 1)(_kv()), nl=1,
+             P=0x4000, par=0x5000, n=0x6000, keep=0x7000, B=2, n_max=16, V=10, Hkv=2, d=128,
+             dt=ta.TA_BF16, path=0x8000, plen=0x9000, bonus=0xa000, ws=0xb000, wsb=1 << 20)
+    a.update(kw)
+    return lib.tree_accept_reroot(a["lg"], a["ldt"], a["tok"], a["rt"], a["arr"], a["nl"], a["P"],
+                                  a["par"], a["n"], a["keep"], a["B"], a["n_max"], a["V"],
+                                  a["Hkv"], a["d"], a["dt"], a["path"], a["plen"], a["bonus"],
+                                  a["ws"], a["wsb"], None)
+
+
+def test_accept_reroot_host_side_validation():
+    """tree_accept_reroot checks what accept_greedy_path and tree_cache_reroot
+    check, plus its workspace, before any launch."""
+    lib = ensure_built()
+    need = ta.tree_accept_reroot_workspace_bytes(2, 16)
+    # argmax per node, copies of parent, prefix_len and n_nodes, each on a
+    # 256-byte boundary
+    assert need == 4 * 256
+    assert ta.tree_accept_reroot_workspace_bytes(100, 256) == 2 * 102400 + 2 * 512
+    assert lib.tree_accept_reroot_workspace_bytes(-1, 16) == ctypes.c_size_t(-1).value
+    assert lib.tree_accept_reroot_workspace_bytes(2, 257) == ctypes.c_size_t(-1).value
+    assert _accept_reroot(lib, n_max=300) == _lib.TA_ERR_TREE_TOO_LARGE
+    assert _accept_reroot(lib, ldt=5) == _lib.TA_ERR_UNSUPPORTED
+    assert _accept_reroot(lib, dt=9) == _lib.TA_ERR_UNSUPPORTED
+    assert _accept_reroot(lib, d=80) == _lib.TA_ERR_UNSUPPORTED
+    assert _accept_reroot(lib, lg=None) == _lib.TA_ERR_INVALID_ARG
+    assert _accept_reroot(lib, keep=None) == _lib.TA_ERR_INVALID_ARG
+    assert _accept_reroot(lib, bonus=None) == _lib.TA_ERR_INVALID_ARG
+    assert _accept_reroot(lib, nl=-1) == _lib.TA_ERR_INVALID_ARG
+    assert _accept_reroot(lib, V=0) == _lib.TA_ERR_INVALID_ARG
+    assert _accept_reroot(lib, arr=None) == _lib.TA_ERR_INVALID_ARG
+    mis = (_lib.ta_kv * 1)(_lib.ta_kv(0x1001, 0x2000, None, 0, 0, 0, 64))
+    assert _accept_reroot(lib, arr=mis) == _lib.TA_ERR_INVALID_ARG
+    assert _accept_reroot(lib, ws=None) == _lib.TA_ERR_WORKSPACE
+    assert _accept_reroot(lib, wsb=need - 1) == _lib.TA_ERR_WORKSPACE
+    assert _accept_reroot(lib, ws=0xb004) == _lib.TA_ERR_WORKSPACE   # not 16-byte aligned
+    assert _accept_reroot(lib, B=0, ws=None) == _lib.TA_OK           # nothing to do
+    assert _accept_reroot(lib, nl=0, arr=None, B=0) == _lib.TA_OK

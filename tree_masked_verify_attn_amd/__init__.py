@@ -12,6 +12,7 @@ entry points keep the C names:
 * ``accept_sampling_path`` -- the same by speculative sampling (temperature > 0)
 * ``tree_cache_reroot``  -- evolving-tree-cache re-root with in-place KV moves
 * ``tree_cache_reroot_draft`` -- the same, moving the draft's tokens and re-based scores too
+* ``tree_accept_reroot`` -- ``accept_greedy_path`` + ``tree_cache_reroot`` in two launches
 * ``tree_expand_top_w``  -- maximum-likelihood expansion: append the w best leaves
 * ``tree_rope_append``   -- RoPE at tree positions + KV append of the new nodes
 * ``tree_token_walk``    -- draft side: walk along the verified tokens (re-root path)
@@ -40,6 +41,8 @@ from ._lib import (  # noqa: F401
     tree_attn_workspace_bytes,
     tree_cache_reroot,
     tree_cache_reroot_draft,
+    tree_accept_reroot,
+    tree_accept_reroot_workspace_bytes,
     tree_expand_top_w,
     tree_expand_top_w_workspace_bytes,
     tree_rope_append,

@@ -39,6 +39,8 @@ EXPORTED_SYMBOLS = (
     "accept_sampling_workspace_bytes",
     "tree_cache_reroot",
     "tree_cache_reroot_draft",
+    "tree_accept_reroot",
+    "tree_accept_reroot_workspace_bytes",
     "tree_expand_top_w",
     "tree_expand_top_w_workspace_bytes",
     "tree_rope_append",
@@ -126,6 +128,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.tree_cache_reroot_draft.argtypes = [ctypes.POINTER(ta_kv), c_int] + [vp] * 8 + \
             [c_int] * 5 + [vp]
         lib.tree_cache_reroot_draft.restype = c_int
+        lib.tree_accept_reroot.argtypes = [vp, c_int, vp, vp, ctypes.POINTER(ta_kv), c_int] + \
+            [vp] * 4 + [c_int] * 6 + [vp] * 4 + [c_size, vp]
+        lib.tree_accept_reroot.restype = c_int
+        lib.tree_accept_reroot_workspace_bytes.argtypes = [c_int, c_int]
+        lib.tree_accept_reroot_workspace_bytes.restype = c_size
         lib.tree_expand_top_w.argtypes = [vp, c_int, vp, vp, vp, vp, c_int, c_int, c_int, c_int,
                                           vp, c_size, vp]
         lib.tree_expand_top_w.restype = c_int
@@ -601,6 +608,69 @@ def tree_cache_reroot_draft(kv_layers: Sequence[KVCache], prefix_len, parent, n_
     and (re-based to the new root) cumulative scores ``cum``, in place."""
     _reroot(kv_layers, prefix_len, parent, n_nodes, path, path_len, keep_subtree, tok, cum,
             stream, True)
+
+
+def tree_accept_reroot_workspace_bytes(B: int, n_max: int) -> int:
+    n = load_library().tree_accept_reroot_workspace_bytes(B, n_max)
+    if n == ctypes.c_size_t(-1).value:
+        raise TreeAttnError(TA_ERR_INVALID_ARG, "invalid sizes for an accept + re-root workspace query")
+    return int(n)
+
+
+def tree_accept_reroot(logits, tok, root_tok, kv_layers: Sequence[KVCache], prefix_len, parent,
+                       n_nodes, keep_subtree, path=None, path_len=None, bonus=None,
+                       workspace=None, stream=None):
+    """accept_greedy_path, then tree_cache_reroot on the path it finds (two
+    launches).  Returns ``(path, path_len, bonus)``; the caches and
+    prefix_len / parent / n_nodes are updated in place.  ``workspace``
+    defaults to the one kept per (device, stream)."""
+    torch = _torch()
+    lib = load_library()
+    _need(logits, "logits", ndim=3)
+    dev = logits.device
+    _need(tok, "tok", dtype=torch.int32, ndim=2, device=dev)
+    _need(root_tok, "root_tok", dtype=torch.int32, ndim=1, device=dev)
+    _need(prefix_len, "prefix_len", dtype=torch.int32, ndim=1, device=dev)
+    _need(parent, "parent", dtype=torch.int32, ndim=2, device=dev)
+    _need(n_nodes, "n_nodes", dtype=torch.int32, ndim=1, device=dev)
+    _need(keep_subtree, "keep_subtree", dtype=torch.uint8, ndim=1, device=dev)
+    B, n_max, V = (int(x) for x in logits.shape)
+    if tuple(parent.shape) != (B, n_max) or tuple(tok.shape) != (B, n_max):
+        raise ValueError("parent/tok must be [B][n_max] matching logits")
+    if path is None:
+        path = torch.empty((B, n_max), dtype=torch.int32, device=dev)
+    if path_len is None:
+        path_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    if bonus is None:
+        bonus = torch.empty((B,), dtype=torch.int32, device=dev)
+    _need(path, "path", dtype=torch.int32, ndim=2, device=dev)
+    _need(path_len, "path_len", dtype=torch.int32, ndim=1, device=dev)
+    _need(bonus, "bonus", dtype=torch.int32, ndim=1, device=dev)
+    if tuple(path.shape) != (B, n_max) or path_len.shape[0] != B or bonus.shape[0] != B:
+        raise ValueError("path must be [B][n_max], path_len and bonus [B]")
+    layers: List[KVCache] = list(kv_layers)
+    if layers:
+        Hkv, d, dtype = layers[0].Hkv, layers[0].d, layers[0].dtype
+        for L in layers:
+            if (L.Hkv, L.d, L.dtype) != (Hkv, d, dtype) or L.k.device != dev:
+                raise ValueError("all layers must share Hkv, d, dtype and device")
+        dt = _dtype_code(layers[0].k)
+    else:
+        Hkv, d, dt = 1, 128, TA_BF16
+    arr = (ta_kv * max(1, len(layers)))(*[L.struct() for L in layers])
+    nbytes = tree_accept_reroot_workspace_bytes(B, n_max)
+    if workspace is None:
+        ws = _workspace_for(dev, nbytes, stream)
+    else:
+        ws = workspace.get(nbytes, dev, _torch_stream(stream, dev))
+    st = lib.tree_accept_reroot(logits.data_ptr(), _dtype_code(logits), tok.data_ptr(),
+                                root_tok.data_ptr(), arr, len(layers), prefix_len.data_ptr(),
+                                parent.data_ptr(), n_nodes.data_ptr(), keep_subtree.data_ptr(), B,
+                                n_max, V, Hkv, d, dt, path.data_ptr(), path_len.data_ptr(),
+                                bonus.data_ptr(), _ptr(ws), nbytes if ws is not None else 0,
+                                _stream(stream))
+    _check(st)
+    return path, path_len, bonus
 
 
 def tree_expand_top_w_workspace_bytes(B: int, n_max: int, w: int) -> int:

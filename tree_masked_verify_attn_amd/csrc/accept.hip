@@ -14,6 +14,7 @@
 //      deepest accepted node (popcount of its mask, lowest index on ties)
 //      wins and its mask, read in index order, is the path.
 #include "ta_device.h"
+#include "tree_walk.h"
 
 namespace ta {
 namespace {
@@ -46,9 +47,18 @@ constexpr int kArgUnroll = 8;
 template <bool kBf16>
 __global__ __launch_bounds__(kArgThreads) void argmax_kernel(const void* logits,
                                                              const int32_t* n_nodes, int n_max,
-                                                             int V, int32_t* path) {
+                                                             int V, int32_t* path,
+                                                             MetaSnapshot snap) {
   const int i = blockIdx.x;
   const int b = blockIdx.y;
+  if (snap.parent != nullptr && i == 0) {  // the sequence's metadata as it is now
+    const size_t row = static_cast<size_t>(b) * n_max;
+    for (int t = threadIdx.x; t < n_max; t += kArgThreads) snap.parent_out[row + t] = snap.parent[row + t];
+    if (threadIdx.x == 0) {
+      snap.prefix_len_out[b] = snap.prefix_len[b];
+      snap.n_nodes_out[b] = n_nodes[b];
+    }
+  }
   int n = n_nodes[b];
   n = n < 0 ? 0 : (n > n_max ? n_max : n);
   if (i >= n) return;
@@ -137,75 +147,36 @@ __global__ __launch_bounds__(kThreads) void accept_path_kernel(const int32_t* pa
   const int tok_i = tok[static_cast<size_t>(b) * n_max + ic];
   n = n < 0 ? 0 : (n > n_max ? n_max : n);
 
-  if (i < n) sA[i] = a_i;
-  if (i < kMaskWords) sAcc[i] = 0;
-  build_ancestor_masks_of(par_i, n, sAnc, sJump);  // synchronises (also after the writes above)
-
-  bool acc = false;
-  if (i < n) {
-    const int p = clamp_parent(par_i, i);
-    acc = tok_i == (p < 0 ? rt : sA[p]);
-  }
-  const unsigned long long bal = __ballot(acc);  // 64 nodes per wave -> mask word (i >> 6)
-  if ((i & 63) == 0) sAcc[i >> 6] = bal;
-  __syncthreads();
-
-  unsigned long long key = 0;  // (depth << 16) | (0xffff - node); 0 = not accepted
-  if (i < n) {
-    bool ok = true;
-    int depth = 0;
-#pragma unroll
-    for (int w = 0; w < kMaskWords; ++w) {
-      ok = ok && ((sAnc[i][w] & ~sAcc[w]) == 0);
-      depth += __popcll(sAnc[i][w]);
-    }
-    if (ok) key = (static_cast<unsigned long long>(depth) << 16) | (0xffffu - i);
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const unsigned long long other = __shfl_xor(key, o, 64);
-    key = other > key ? other : key;
-  }
-  if ((i & 63) == 0) sKey[i >> 6] = key;
-  __syncthreads();
-  unsigned long long best_key = sKey[0];
-#pragma unroll
-  for (int w = 1; w < kThreads / 64; ++w) best_key = sKey[w] > best_key ? sKey[w] : best_key;
-
-  const int best = best_key ? static_cast<int>(0xffffu - (best_key & 0xffffu)) : -1;
-  const int len = best_key ? static_cast<int>(best_key >> 16) : 0;
+  const Accepted r = greedy_accept(n, rt, a_i, par_i, tok_i, sAnc, sJump, sA, sAcc, sKey);
   // Write the path: node j of best's mask goes to slot popcount(mask below j).
   if (i < n_max) {
-    int slot = -1;
-    if (best >= 0 && i < n && mask_bit(sAnc[best], i)) {
-      slot = 0;
-      for (int w = 0; w < kMaskWords; ++w) {
-        const uint64_t m = sAnc[best][w];
-        if (w < (i >> 6))
-          slot += __popcll(m);
-        else if (w == (i >> 6))
-          slot += __popcll(m & ((1ull << (i & 63)) - 1ull));
-      }
-    }
+    const int slot = path_slot(sAnc, r.best, i, n);
     if (slot >= 0) path_b[slot] = i;
-    if (i >= len) path_b[i] = -1;
+    if (i >= r.len) path_b[i] = -1;
   }
   if (i == 0) {
-    path_len[b] = len;
-    bonus[b] = best >= 0 ? sA[best] : rt;
+    path_len[b] = r.len;
+    bonus[b] = r.best >= 0 ? sA[r.best] : rt;
   }
 }
 
 }  // namespace
 
+hipError_t launch_argmax(const void* logits, int logit_dtype, const int32_t* n_nodes, int B,
+                         int n_max, int V, int32_t* out, const MetaSnapshot& snap, hipStream_t s) {
+  dim3 g1(n_max, B);
+  return logit_dtype == TA_BF16
+             ? launch(argmax_kernel<true>, g1, dim3(kArgThreads), s, logits, n_nodes, n_max, V, out,
+                      snap)
+             : launch(argmax_kernel<false>, g1, dim3(kArgThreads), s, logits, n_nodes, n_max, V, out,
+                      snap);
+}
+
 hipError_t launch_accept(const void* logits, int logit_dtype, const int32_t* parent,
                          const int32_t* tok, const int32_t* n_nodes, const int32_t* root_tok,
                          int B, int n_max, int V, int32_t* path, int32_t* path_len,
                          int32_t* bonus, hipStream_t s) {
-  dim3 g1(n_max, B);
-  hipError_t e = logit_dtype == TA_BF16
-                     ? launch(argmax_kernel<true>, g1, dim3(kArgThreads), s, logits, n_nodes, n_max, V, path)
-                     : launch(argmax_kernel<false>, g1, dim3(kArgThreads), s, logits, n_nodes, n_max, V, path);
+  hipError_t e = launch_argmax(logits, logit_dtype, n_nodes, B, n_max, V, path, MetaSnapshot{}, s);
   if (e != hipSuccess) return e;
   return launch(accept_path_kernel, dim3(B), dim3(kThreads), s, parent, tok, n_nodes, root_tok,
                 n_max, path, path_len, bonus);

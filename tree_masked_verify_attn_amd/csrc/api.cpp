@@ -60,6 +60,15 @@ struct Plan {
 
 int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
+// tree_accept_reroot's workspace: the argmax per node, the copy of parent,
+// then of prefix_len and of n_nodes (each on its own 256-byte boundary).
+size_t accept_reroot_region(size_t bytes) { return (bytes + 255) / 256 * 256; }
+size_t accept_reroot_ws_bytes(int B, int n_max) {
+  const size_t rows = static_cast<size_t>(B) * n_max * sizeof(int32_t);
+  const size_t seq = static_cast<size_t>(B) * sizeof(int32_t);
+  return 2 * accept_reroot_region(rows) + 2 * accept_reroot_region(seq);
+}
+
 // Chooses the kernel, the row tiling and the split-KV chunk.  The automatic
 // chunk gives about two work groups per compute unit, never below 256 KV
 // positions per split (smaller chunks cost more in partial results than they
@@ -533,6 +542,65 @@ int tree_cache_reroot_draft(const ta_kv* kv_layers, int n_layers, int32_t* prefi
   if (tok == nullptr) return TA_ERR_INVALID_ARG;
   return reroot_call(kv_layers, n_layers, prefix_len, parent, n_nodes, path, path_len,
                      keep_subtree, tok, cum, B, n_max, Hkv, d, dtype, stream);
+}
+
+size_t tree_accept_reroot_workspace_bytes(int B, int n_max) {
+  if (B < 0 || n_max < 1 || n_max > TA_MAX_NODES) return static_cast<size_t>(-1);
+  return accept_reroot_ws_bytes(B, n_max);
+}
+
+int tree_accept_reroot(const void* logits, int logit_dtype, const int32_t* tok,
+                       const int32_t* root_tok, const ta_kv* kv_layers, int n_layers,
+                       int32_t* prefix_len, int32_t* parent, int32_t* n_nodes,
+                       const uint8_t* keep_subtree, int B, int n_max, int V, int Hkv, int d,
+                       int dtype, int32_t* path, int32_t* path_len, int32_t* bonus, void* ws,
+                       size_t ws_bytes, void* stream) {
+  if (B < 0 || n_max < 1 || V < 1 || n_layers < 0 || Hkv < 1) return TA_ERR_INVALID_ARG;
+  if (n_max > TA_MAX_NODES) return TA_ERR_TREE_TOO_LARGE;
+  if (logit_dtype != TA_F32 && logit_dtype != TA_BF16) return TA_ERR_UNSUPPORTED;
+  if (dtype != TA_F32 && dtype != TA_BF16) return TA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return TA_ERR_UNSUPPORTED;
+  if (logits == nullptr || tok == nullptr || root_tok == nullptr || prefix_len == nullptr ||
+      parent == nullptr || n_nodes == nullptr || keep_subtree == nullptr || path == nullptr ||
+      path_len == nullptr || bonus == nullptr || (n_layers > 0 && kv_layers == nullptr))
+    return TA_ERR_INVALID_ARG;
+  for (int i = 0; i < n_layers; ++i) {
+    const int st = check_kv(kv_layers[i]);
+    if (st != TA_OK) return st;
+    if (!aligned16(kv_layers[i].k) || !aligned16(kv_layers[i].v)) return TA_ERR_INVALID_ARG;
+  }
+  if (B == 0) return TA_OK;
+  if (ws == nullptr || ws_bytes < accept_reroot_ws_bytes(B, n_max) || !aligned16(ws))
+    return TA_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  const size_t rows = accept_reroot_region(static_cast<size_t>(B) * n_max * sizeof(int32_t));
+  const size_t seq = accept_reroot_region(static_cast<size_t>(B) * sizeof(int32_t));
+  int32_t* amax = reinterpret_cast<int32_t*>(w);
+  ta::MetaSnapshot snap{prefix_len, parent, reinterpret_cast<int32_t*>(w + 2 * rows),
+                        reinterpret_cast<int32_t*>(w + 2 * rows + seq),
+                        reinterpret_cast<int32_t*>(w + rows)};
+  hipError_t e = ta::launch_argmax(logits, logit_dtype, n_nodes, B, n_max, V, amax, snap, s);
+  if (e != hipSuccess) return hip_status(e, "tree_accept_reroot argmax launch");
+  const int row_bytes = d * (dtype == TA_BF16 ? 2 : 4);
+  // Every launch takes the path itself from the snapshot; the first writes
+  // the path and the new metadata out.
+  int l0 = 0;
+  do {
+    const int cnt = std::min(ta::kRerootMaxLayersPerLaunch, n_layers - l0);
+    ta::RerootLayers L{};
+    for (int i = 0; i < cnt; ++i) {
+      const ta_kv& kv = kv_layers[l0 + i];
+      L.l[i] = ta::RerootLayer{kv.k, kv.v, kv.block_table, kv.block_size, kv.max_blocks,
+                               kv.num_blocks, kv.T_cap};
+    }
+    e = ta::launch_accept_reroot(L, cnt, prefix_len, parent, n_nodes, snap, tok, root_tok, amax,
+                                 keep_subtree, B, n_max, Hkv, row_bytes, path, path_len, bonus,
+                                 l0 == 0 ? 1 : 0, s);
+    if (e != hipSuccess) return hip_status(e, "tree_accept_reroot launch");
+    l0 += cnt;
+  } while (l0 < n_layers);
+  return TA_OK;
 }
 
 size_t tree_expand_top_w_workspace_bytes(int B, int n_max, int w) {

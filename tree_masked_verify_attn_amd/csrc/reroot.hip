@@ -15,7 +15,15 @@
 // Launch 2 (metadata): one work group per sequence rewrites parent, n_nodes
 // and prefix_len after every layer has been moved (stream order), and moves
 // the draft's per-node tokens and weights when it is given them.
+//
+// Fused with the greedy acceptance (accept_reroot_kernel): the same move
+// groups first take the accepted path themselves (tree_walk.h) from the
+// target's argmax per node, so no launch has to hand the path over; and they
+// read the tree from a copy the argmax launch took, so one of them can
+// rewrite the live metadata at once instead of a separate launch after the
+// moves.
 #include "ta_device.h"
+#include "tree_walk.h"
 
 namespace ta {
 namespace {
@@ -27,6 +35,22 @@ constexpr int kMaxChunksPerThread = kMaxNodes * kSliceChunks / kThreads;
 struct Plan {
   int P, n, k, keep, v_last, n_kept, valid;
 };
+
+// The kept set: descendants of the path's last node when the subtree is
+// kept (a 256-bit mask in sKept), and its size.  Synchronises.
+__device__ __forceinline__ void plan_kept(Plan& pl, const uint64_t (*sAnc)[kMaskWords],
+                                          uint64_t* sKept) {
+  const int tid = threadIdx.x;
+  bool kept = false;
+  if (pl.keep && pl.k > 0 && tid < pl.n && tid != pl.v_last) kept = mask_bit(sAnc[tid], pl.v_last);
+  const unsigned long long bal = __ballot(kept);
+  if ((tid & 63) == 0) sKept[tid >> 6] = bal;
+  __syncthreads();
+  int nk = 0;
+#pragma unroll
+  for (int w = 0; w < kMaskWords; ++w) nk += __popcll(sKept[w]);
+  pl.n_kept = nk;
+}
 
 // Shared by both launches: sequence bounds, path, kept set (as a 256-bit mask
 // in sKept) and each kept node's rank (popcount of kept bits below it).
@@ -58,15 +82,7 @@ __device__ __forceinline__ Plan make_plan(const int32_t* prefix_len, const int32
   if (tid < kMaskWords) sKept[tid] = 0;
   build_ancestor_masks_of(par_i, n, sAnc, sJump);
   pl.v_last = k > 0 ? sPath[k - 1] : -1;
-  bool kept = false;
-  if (pl.keep && k > 0 && tid < n && tid != pl.v_last) kept = mask_bit(sAnc[tid], pl.v_last);
-  const unsigned long long bal = __ballot(kept);
-  if ((tid & 63) == 0) sKept[tid >> 6] = bal;
-  __syncthreads();
-  int nk = 0;
-#pragma unroll
-  for (int w = 0; w < kMaskWords; ++w) nk += __popcll(sKept[w]);
-  pl.n_kept = nk;
+  plan_kept(pl, sAnc, sKept);
   return pl;
 }
 
@@ -82,30 +98,14 @@ __device__ __forceinline__ int kept_rank(const uint64_t* sKept, int i) {
   return r;
 }
 
-__global__ __launch_bounds__(kThreads) void reroot_move_kernel(
-    RerootLayers layers, int n_layers, const int32_t* prefix_len, const int32_t* parent,
-    const int32_t* n_nodes, const int32_t* path, const int32_t* path_len, const uint8_t* keep,
-    int n_max, int Hkv, int row_bytes) {
-  __shared__ uint64_t sAnc[kMaxNodes][kMaskWords];
-  __shared__ int sJump[kMaxNodes];
-  __shared__ uint64_t sKept[kMaskWords];
-  __shared__ int sPath[kMaxNodes];
-  __shared__ int sSrc[kMaxNodes];
-  __shared__ int sDst[kMaxNodes];
-
-  const int n_slices = row_bytes / (16 * kSliceChunks);
-  const int hkv = blockIdx.x / n_slices;
-  const int slice = blockIdx.x % n_slices;
-  const int which = blockIdx.y;  // 0: K, 1: V
-  const int b = blockIdx.z / n_layers;
-  const int layer = blockIdx.z % n_layers;
+// Copies this work group's 64-byte column slice (K or V of one KV head of one
+// layer of sequence b) of every row that changes place.  All threads call it
+// (it synchronises); it stops early when no row moves.
+__device__ __forceinline__ void move_slice(const RerootLayer& L, int b, int hkv, int which,
+                                           int slice, int Hkv, int row_bytes, const Plan& pl,
+                                           const int* sPath, const uint64_t* sKept, int* sSrc,
+                                           int* sDst) {
   const int tid = threadIdx.x;
-  const RerootLayer& L = layers.l[layer];
-
-  const Plan pl = make_plan(prefix_len, parent, n_nodes, path, path_len, keep, b, n_max, sAnc,
-                            sJump, sKept, sPath);
-  if (!pl.valid || pl.k == 0) return;  // nothing moves (keep: no-op; drop: metadata only)
-
   // Move list: slot j < k promotes path node j; slot k + r takes kept node of rank r.
   const int n_moves = min(pl.k + pl.n_kept, kMaxNodes);
   if (tid < pl.k) {
@@ -168,34 +168,24 @@ __global__ __launch_bounds__(kThreads) void reroot_move_kernel(
   store(3, r3);
 }
 
-// tok / cum (either may be null): per-node arrays the draft keeps beside its
-// tree.  They move with their nodes; cum is re-based to the new root (the last
-// verified node), whose own weight is subtracted.  Entries at or past the new
-// node count read -1 / -inf.
-__global__ __launch_bounds__(kThreads) void reroot_meta_kernel(int32_t* prefix_len,
-                                                               int32_t* parent, int32_t* n_nodes,
-                                                               const int32_t* path,
-                                                               const int32_t* path_len,
-                                                               const uint8_t* keep, int n_max,
-                                                               int32_t* tok, float* cum) {
-  __shared__ uint64_t sAnc[kMaxNodes][kMaskWords];
-  __shared__ int sJump[kMaxNodes];
-  __shared__ uint64_t sKept[kMaskWords];
-  __shared__ int sPath[kMaxNodes];
-  const int b = blockIdx.x;
+// The metadata of sequence b after the move: kept node of rank r takes slot
+// r, with its parent renumbered (-1 under the new root); the path's nodes
+// join the prefix.  par_tid: the old parent entry of node tid (tid < n).
+// tok_b / cum_b (either may be null): per-node arrays the draft keeps beside
+// its tree.  They move with their nodes; cum is re-based to the new root (the
+// last verified node), whose own weight is subtracted.  Entries at or past
+// the new node count read -1 / -inf.  All threads call it (it synchronises):
+// every old value is read before the first write.
+__device__ __forceinline__ void rewrite_meta(const Plan& pl, int par_tid, int b, int n_max,
+                                             int32_t* prefix_len, int32_t* par_b,
+                                             int32_t* n_nodes, int32_t* tok_b, float* cum_b,
+                                             const uint64_t* sKept) {
   const int tid = threadIdx.x;
-  int32_t* par_b = parent + static_cast<size_t>(b) * n_max;
-  int32_t* tok_b = tok != nullptr ? tok + static_cast<size_t>(b) * n_max : nullptr;
-  float* cum_b = cum != nullptr ? cum + static_cast<size_t>(b) * n_max : nullptr;
-  const Plan pl = make_plan(prefix_len, parent, n_nodes, path, path_len, keep, b, n_max, sAnc,
-                            sJump, sKept, sPath);
-  if (!pl.valid || (pl.k == 0 && pl.keep)) return;
-  // Read every old parent, token and weight before any write.
   int newpar = -1, slot = -1, tk = -1;
   float w = 0.f;
   const float base = (cum_b != nullptr && pl.v_last >= 0) ? cum_b[pl.v_last] : 0.f;
   if (tid < pl.n && mask_bit(sKept, tid)) {
-    const int pp = clamp_parent(par_b[tid], tid);
+    const int pp = clamp_parent(par_tid, tid);
     slot = kept_rank(sKept, tid);
     newpar = (pp == pl.v_last || pp < 0) ? -1 : kept_rank(sKept, pp);
     if (tok_b != nullptr) tk = tok_b[tid];
@@ -218,6 +208,126 @@ __global__ __launch_bounds__(kThreads) void reroot_meta_kernel(int32_t* prefix_l
   }
 }
 
+__global__ __launch_bounds__(kThreads) void reroot_move_kernel(
+    RerootLayers layers, int n_layers, const int32_t* prefix_len, const int32_t* parent,
+    const int32_t* n_nodes, const int32_t* path, const int32_t* path_len, const uint8_t* keep,
+    int n_max, int Hkv, int row_bytes) {
+  __shared__ uint64_t sAnc[kMaxNodes][kMaskWords];
+  __shared__ int sJump[kMaxNodes];
+  __shared__ uint64_t sKept[kMaskWords];
+  __shared__ int sPath[kMaxNodes];
+  __shared__ int sSrc[kMaxNodes];
+  __shared__ int sDst[kMaxNodes];
+
+  const int n_slices = row_bytes / (16 * kSliceChunks);
+  const int hkv = blockIdx.x / n_slices;
+  const int slice = blockIdx.x % n_slices;
+  const int which = blockIdx.y;  // 0: K, 1: V
+  const int b = blockIdx.z / n_layers;
+  const int layer = blockIdx.z % n_layers;
+
+  const Plan pl = make_plan(prefix_len, parent, n_nodes, path, path_len, keep, b, n_max, sAnc,
+                            sJump, sKept, sPath);
+  if (!pl.valid || pl.k == 0) return;  // nothing moves (keep: no-op; drop: metadata only)
+  move_slice(layers.l[layer], b, hkv, which, slice, Hkv, row_bytes, pl, sPath, sKept, sSrc, sDst);
+}
+
+__global__ __launch_bounds__(kThreads) void reroot_meta_kernel(int32_t* prefix_len,
+                                                               int32_t* parent, int32_t* n_nodes,
+                                                               const int32_t* path,
+                                                               const int32_t* path_len,
+                                                               const uint8_t* keep, int n_max,
+                                                               int32_t* tok, float* cum) {
+  __shared__ uint64_t sAnc[kMaxNodes][kMaskWords];
+  __shared__ int sJump[kMaxNodes];
+  __shared__ uint64_t sKept[kMaskWords];
+  __shared__ int sPath[kMaxNodes];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  int32_t* par_b = parent + static_cast<size_t>(b) * n_max;
+  const Plan pl = make_plan(prefix_len, parent, n_nodes, path, path_len, keep, b, n_max, sAnc,
+                            sJump, sKept, sPath);
+  if (!pl.valid || (pl.k == 0 && pl.keep)) return;
+  const int par_tid = tid < pl.n ? par_b[tid] : -1;
+  rewrite_meta(pl, par_tid, b, n_max, prefix_len, par_b, n_nodes,
+               tok != nullptr ? tok + static_cast<size_t>(b) * n_max : nullptr,
+               cum != nullptr ? cum + static_cast<size_t>(b) * n_max : nullptr, sKept);
+}
+
+// Greedy acceptance, re-root move and metadata in one launch (grid as the
+// move launch; with no layers, one group per sequence).  Every group reads the
+// tree from the snapshot the argmax launch took (snap: prefix_len, parent,
+// n_nodes before this call) and amax [B][n_max], the target's argmax per
+// node.  first: this is the call's first launch; its (slice 0, K, layer 0)
+// groups write path / path_len / bonus and the new metadata into the live
+// arrays, which no group of any launch of the call reads.
+__global__ __launch_bounds__(kThreads) void accept_reroot_kernel(
+    RerootLayers layers, int n_layers, int32_t* prefix_len, int32_t* parent, int32_t* n_nodes,
+    MetaSnapshot snap, const int32_t* tok, const int32_t* root_tok, const int32_t* amax,
+    const uint8_t* keep, int n_max, int Hkv, int row_bytes, int32_t* path, int32_t* path_len,
+    int32_t* bonus, int first) {
+  __shared__ uint64_t sAnc[kMaxNodes][kMaskWords];
+  __shared__ int sJump[kMaxNodes];
+  __shared__ uint64_t sKept[kMaskWords];
+  __shared__ int sPath[kMaxNodes];
+  __shared__ int sSrc[kMaxNodes];
+  __shared__ int sDst[kMaxNodes];
+  __shared__ int sA[kMaxNodes];
+  __shared__ uint64_t sAcc[kMaskWords];
+  __shared__ unsigned long long sKey[kThreads / 64];
+  static_assert(kThreads == kWalkThreads, "one thread per node slot");
+
+  const bool moves = n_layers > 0;
+  const int nl = moves ? n_layers : 1;
+  const int n_slices = row_bytes / (16 * kSliceChunks);
+  const int hkv = moves ? blockIdx.x / n_slices : 0;
+  const int slice = moves ? blockIdx.x % n_slices : 0;
+  const int which = blockIdx.y;  // 0: K, 1: V
+  const int b = blockIdx.z / nl;
+  const int layer = blockIdx.z % nl;
+  const int tid = threadIdx.x;
+  const bool writer = first && blockIdx.x == 0 && blockIdx.y == 0 && layer == 0;
+
+  // every global load first (slot index clamped)
+  const int ic = tid < n_max ? tid : n_max - 1;
+  const size_t row = static_cast<size_t>(b) * n_max;
+  int n = snap.n_nodes_out[b];
+  const int P = snap.prefix_len_out[b];
+  const int kp = keep[b];
+  const int rt = root_tok[b];
+  const int a_i = amax[row + ic];
+  const int par_i = snap.parent_out[row + ic];
+  const int tok_i = tok[row + ic];
+  n = n < 0 ? 0 : (n > n_max ? n_max : n);
+
+  const Accepted r = greedy_accept(n, rt, a_i, par_i, tok_i, sAnc, sJump, sA, sAcc, sKey);
+  const int pslot = path_slot(sAnc, r.best, tid, n);
+  if (pslot >= 0) sPath[pslot] = tid;
+  if (writer) {
+    int32_t* path_b = path + row;
+    if (tid < n_max) {
+      if (pslot >= 0) path_b[pslot] = tid;
+      if (tid >= r.len) path_b[tid] = -1;
+    }
+    if (tid == 0) {
+      path_len[b] = r.len;
+      bonus[b] = r.best >= 0 ? sA[r.best] : rt;
+    }
+  }
+  Plan pl;
+  pl.P = P;
+  pl.n = n;
+  pl.k = r.len;
+  pl.keep = kp != 0;
+  pl.valid = P >= 0;
+  pl.v_last = r.len > 0 ? r.best : -1;
+  plan_kept(pl, sAnc, sKept);  // synchronises (sPath complete)
+  if (writer && pl.valid && !(pl.k == 0 && pl.keep))
+    rewrite_meta(pl, par_i, b, n_max, prefix_len, parent + row, n_nodes, nullptr, nullptr, sKept);
+  if (!moves || !pl.valid || pl.k == 0) return;
+  move_slice(layers.l[layer], b, hkv, which, slice, Hkv, row_bytes, pl, sPath, sKept, sSrc, sDst);
+}
+
 }  // namespace
 
 hipError_t launch_reroot_move(const RerootLayers& layers, int n_layers, const int32_t* prefix_len,
@@ -235,6 +345,20 @@ hipError_t launch_reroot_meta(int32_t* prefix_len, int32_t* parent, int32_t* n_n
                               int B, int n_max, int32_t* tok, float* cum, hipStream_t s) {
   return launch(reroot_meta_kernel, dim3(B), dim3(kThreads), s, prefix_len, parent, n_nodes, path,
                 path_len, keep, n_max, tok, cum);
+}
+
+hipError_t launch_accept_reroot(const RerootLayers& layers, int n_layers, int32_t* prefix_len,
+                                int32_t* parent, int32_t* n_nodes, const MetaSnapshot& snap,
+                                const int32_t* tok, const int32_t* root_tok, const int32_t* amax,
+                                const uint8_t* keep, int B, int n_max, int Hkv, int row_bytes,
+                                int32_t* path, int32_t* path_len, int32_t* bonus, int first,
+                                hipStream_t s) {
+  // with no layers, one group per sequence; else the move launch's grid
+  const dim3 grid = n_layers > 0 ? dim3(Hkv * (row_bytes / (16 * kSliceChunks)), 2, B * n_layers)
+                                 : dim3(1, 1, B);
+  return launch(accept_reroot_kernel, grid, dim3(kThreads), s, layers, n_layers, prefix_len,
+                parent, n_nodes, snap, tok, root_tok, amax, keep, n_max, Hkv, row_bytes, path,
+                path_len, bonus, first);
 }
 
 }  // namespace ta

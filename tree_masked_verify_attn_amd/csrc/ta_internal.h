@@ -114,6 +114,20 @@ hipError_t launch_attn_units(const AttnParams& p, hipStream_t s);
 hipError_t launch_attn_merge_units(const AttnParams& p, hipStream_t s);
 
 // Accept: argmax pass (writes a[i] into path) then the path pass.
+// A copy of the tree metadata taken by the argmax launch (parent == nullptr:
+// none), so that the launch after it can rewrite the live arrays while its
+// other work groups still read the old values from the copy.
+struct MetaSnapshot {
+  const int32_t* prefix_len;
+  const int32_t* parent;
+  int32_t* prefix_len_out;  // [B]
+  int32_t* n_nodes_out;     // [B]
+  int32_t* parent_out;      // [B][n_max]
+};
+// argmax of every node's logits row (lowest index on ties) into out [B][n_max]
+// (and the snapshot of the metadata).
+hipError_t launch_argmax(const void* logits, int logit_dtype, const int32_t* n_nodes, int B,
+                         int n_max, int V, int32_t* out, const MetaSnapshot& snap, hipStream_t s);
 hipError_t launch_accept(const void* logits, int logit_dtype, const int32_t* parent,
                          const int32_t* tok, const int32_t* n_nodes, const int32_t* root_tok,
                          int B, int n_max, int V, int32_t* path, int32_t* path_len,
@@ -185,5 +199,13 @@ hipError_t launch_reroot_move(const RerootLayers& layers, int n_layers,
 hipError_t launch_reroot_meta(int32_t* prefix_len, int32_t* parent, int32_t* n_nodes,
                               const int32_t* path, const int32_t* path_len, const uint8_t* keep,
                               int B, int n_max, int32_t* tok, float* cum, hipStream_t s);
+// Greedy acceptance + re-root of a group of layers in one launch (see
+// reroot.hip); amax holds the target's argmax per node (launch_argmax).
+hipError_t launch_accept_reroot(const RerootLayers& layers, int n_layers, int32_t* prefix_len,
+                                int32_t* parent, int32_t* n_nodes, const MetaSnapshot& snap,
+                                const int32_t* tok, const int32_t* root_tok, const int32_t* amax,
+                                const uint8_t* keep, int B, int n_max, int Hkv, int row_bytes,
+                                int32_t* path, int32_t* path_len, int32_t* bonus, int first,
+                                hipStream_t s);
 
 }  // namespace ta
