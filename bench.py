@@ -37,9 +37,12 @@ Other workloads (``--workload``), each printing the same kind of line:
                      tree_cache_reroot_draft, tree_select_subtree).
 
 Prints one JSON line (metric, value = microseconds per step, roofline of the
-attention call, CPU-oracle baseline on a bounded sample).
+attention call, CPU-oracle baseline on a bounded sample).  Without
+--workload the line is chain_verify's, and the other three workloads are
+timed after it in the same process and reported under "other_workloads"
+(their step, attention call and HBM fraction; not part of value).
 
-    python bench.py [--workload W] [--steps K] [--warmup W] [--eager] [--no-cpu-baseline]
+    python bench.py [--workload W] [--steps K] [--warmup W] [--eager] [--no-cpu-baseline] [--no-others]
     python bench.py --copy-calib     # plain device copy of known size (PMC scaling)
 """
 from __future__ import annotations
@@ -59,6 +62,12 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD's published peak
 METRIC = "tree-verify attention µs/step + achieved KV-read GB/s (% of MI355X HBM peak)"
 WORKLOADS = ("chain_verify", "paged_alternating", "tree_verify_l70b", "draft_expand")
+OTHER_WORKLOADS = WORKLOADS[1:]  # timed beside the default workload's line
+
+
+def r_phase0(r):
+    """Name of a result's first phase (the attention calls)."""
+    return "verify" if "verify_us" in r else "expand"
 PHASE_REPS = 5                  # timed replays of each single-phase graph
 MIN_TIMED_CALLS = 50            # individually timed calls per phase (per-call percentiles)
 
@@ -691,52 +700,15 @@ def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
     return nbytes, sorted(t)[len(t) // 2]
 
 
-def main(argv=None):
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=WORKLOADS, default="chain_verify")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
-    ap.add_argument("--copy-calib", action="store_true",
-                    help="only run a 1 GiB device copy (for PMC byte-counter scaling)")
-    ap.add_argument("--kernel", type=int, default=0,
-                    help="0 auto, 1 generic, 2 MFMA (register prefetch), 3 MFMA (LDS-DMA ring)")
-    ap.add_argument("--chunk", type=int, default=0, help="KV positions per split (0 = auto)")
-    ap.add_argument("--eager", action="store_true",
-                    help="issue every call from Python inside the timed region (no HIP graph)")
-    a = ap.parse_args(argv)
-
-    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: the library has no multi-GPU path "
-              "(the verify kernel shards by (sequence, KV head) with no exchange; "
-              "run with --gpus 1)", file=sys.stderr)
-        sys.exit(2)
-
+def measure(ta, workload, a, dev):
+    """Builds one workload, runs the warm-up, times a.steps steps and each
+    phase; returns the JSON fields (no CPU baseline) and the workload."""
     import numpy as np
     import torch
 
-    import tree_masked_verify_attn_amd as ta
-    from tree_masked_verify_attn_amd import build as tb
-
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    if not os.path.exists(tb.LIB):
-        tb.build()
-    ta.load_library()
-
-    if a.copy_calib:
-        nbytes, sec = copy_calibration()
-        print(json.dumps({"copy_bytes": nbytes, "copy_s": sec,
-                          "copy_GBps": 2 * nbytes / sec / 1e9}), flush=True)
-        return
-
-    dev = torch.device("cuda:0")
     t0 = time.time()
-    w = RUNNERS[a.workload](ta, _Up(dev))
-    _log(f"generated {a.workload} inputs in {time.time() - t0:.1f} s")
+    w = RUNNERS[workload](ta, _Up(dev))
+    _log(f"generated {workload} inputs in {time.time() - t0:.1f} s")
     ws = ta.Workspace(dev)
     opts = {"kernel": a.kernel, "chunk_tokens": a.chunk}
     torch.cuda.synchronize()
@@ -855,7 +827,7 @@ def main(argv=None):
     call = "tree_attn_verify" if w.phases[0] == "verify" else "4 tree_attn_expand calls"
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": read_traffic(a.workload),
+                "traffic": read_traffic(workload),
                 "kernel": f"{call} (attention kernel + split-combine kernel when split)",
                 "algorithmic_bytes_per_launch": int(np.mean([b["total"] for b in steps_bytes])),
                 "avg_launch_us": round(attn_s * 1e6, 2)}
@@ -893,6 +865,60 @@ def main(argv=None):
         res["beside_step"] = sorted(f"{name}_us" for name in extra_ms)
     res["device_copy_GBps"] = round(2 * (1 << 30) / copy_s / 1e9, 1)
     res["roofline"] = roofline
+    return res, w
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", choices=WORKLOADS, default=None,
+                    help="the workload of the line (default chain_verify, with the other "
+                         "workloads timed beside it)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-others", action="store_true",
+                    help="without --workload: skip timing the other workloads beside chain_verify")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="only run a 1 GiB device copy (for PMC byte-counter scaling)")
+    ap.add_argument("--kernel", type=int, default=0,
+                    help="0 auto, 1 generic, 2 MFMA (register prefetch), 3 MFMA (LDS-DMA ring)")
+    ap.add_argument("--chunk", type=int, default=0, help="KV positions per split (0 = auto)")
+    ap.add_argument("--eager", action="store_true",
+                    help="issue every call from Python inside the timed region (no HIP graph)")
+    a = ap.parse_args(argv)
+    others_too = a.workload is None and not a.no_others
+    if a.workload is None:
+        a.workload = "chain_verify"
+
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(the verify kernel shards by (sequence, KV head) with no exchange; "
+              "run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import tree_masked_verify_attn_amd as ta
+    from tree_masked_verify_attn_amd import build as tb
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if not os.path.exists(tb.LIB):
+        tb.build()
+    ta.load_library()
+
+    if a.copy_calib:
+        nbytes, sec = copy_calibration()
+        print(json.dumps({"copy_bytes": nbytes, "copy_s": sec,
+                          "copy_GBps": 2 * nbytes / sec / 1e9}), flush=True)
+        return
+
+    dev = torch.device("cuda:0")
+    res, w = measure(ta, a.workload, a, dev)
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = w.cpu_baseline(a.cpu_budget)
         # the same oracle on one core (BLAS limited to one thread)
@@ -904,6 +930,24 @@ def main(argv=None):
             with threadpool_limits(limits=1):
                 one = w.cpu_baseline(a.cpu_budget)
             res["cpu_baseline_1core"] = one
+    if others_too:
+        # The other single-GPU workloads, timed the same way in this process
+        # (not part of value): their step time, the attention call and its
+        # HBM fraction.
+        del w
+        torch.cuda.empty_cache()
+        others = {}
+        for name in OTHER_WORKLOADS:
+            r, w2 = measure(ta, name, a, dev)
+            first = f"{r_phase0(r)}_us"
+            others[name] = {"value": r["value"], "unit": r["unit"], first: r[first],
+                            **{k: v for k, v in r.items() if k.endswith("_us") and k != first},
+                            "roofline": {k: r["roofline"][k] for k in
+                                         ("achieved", "frac", "traffic", "avg_launch_us")},
+                            "config": r["config"]}
+            del w2, r
+            torch.cuda.empty_cache()
+        res["other_workloads"] = others
     print(json.dumps(res), flush=True)
 
 
