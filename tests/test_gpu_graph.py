@@ -31,8 +31,12 @@ def _bits(t):
     return t.cpu().numpy()
 
 
-@pytest.mark.parametrize("paged", [False, True])
-def test_step_graph_replays_match_eager(ta, paged):
+@pytest.mark.parametrize("paged,fused", [(False, False), (True, False), (False, True),
+                                         (True, True)])
+def test_step_graph_replays_match_eager(ta, paged, fused):
+    """fused: greedy accept + re-root through tree_accept_reroot (two
+    launches, its copy of the metadata in the shared workspace), else
+    accept_greedy_path then tree_cache_reroot."""
     import torch
     c = random_case(41 + int(paged), B=5, Hq=16, Hkv=2, d=128, P_range=(0, 1500), n_max=24,
                     dtype="bf16", paged=paged, vocab=3000)
@@ -63,9 +67,13 @@ def test_step_graph_replays_match_eager(ta, paged):
                             lse=lse, workspace=ws, **opts)
         ta.tree_attn_expand(q_exp, dc.kv, dc.prefix_len, dc.parent, dc.n_nodes, c.scale,
                             out=out_x, lse=lse_x, workspace=ws, **opts)
-        ta.accept_greedy_path(dc.logits, dc.parent, dc.tok, dc.n_nodes, dc.root_tok, path, plen,
-                              bonus)
-        ta.tree_cache_reroot([dc.kv], dc.prefix_len, dc.parent, dc.n_nodes, path, plen, keep)
+        if fused:
+            ta.tree_accept_reroot(dc.logits, dc.tok, dc.root_tok, [dc.kv], dc.prefix_len,
+                                  dc.parent, dc.n_nodes, keep, path, plen, bonus, workspace=ws)
+        else:
+            ta.accept_greedy_path(dc.logits, dc.parent, dc.tok, dc.n_nodes, dc.root_tok, path,
+                                  plen, bonus)
+            ta.tree_cache_reroot([dc.kv], dc.prefix_len, dc.parent, dc.n_nodes, path, plen, keep)
 
     def results():
         torch.cuda.synchronize()
