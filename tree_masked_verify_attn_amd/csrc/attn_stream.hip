@@ -65,26 +65,77 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
   const int wave = tid >> 6;
   const int lhi = lane >> 5;
   const int l32 = lane & 31;
-
-  SeqBounds sb;
-  if (!seq_bounds(p.prefix_len, p.n_nodes, b, p.n_max, p.T_cap, sb)) return;
-  const int nsplit = (sb.T + p.chunk - 1) / p.chunk;
-  if (split >= nsplit) return;
   const int t_begin = split * p.chunk;
-  const int t_end = min(sb.T, t_begin + p.chunk);
+  const uint8_t* Kg = static_cast<const uint8_t*>(p.k);
+  const uint8_t* Vg = static_cast<const uint8_t*>(p.v);
+  const uint32_t ring_base = static_cast<uint32_t>(reinterpret_cast<size_t>((lds_u8*)sRing));
+  const size_t pos_stride = static_cast<size_t>(p.Hkv) * C::ROW;  // contiguous: bytes per position
 
   const int rg = wave < NRG ? wave : -1;  // computing waves own one 32-row group each
   const int R = p.n_q * p.G;
   const int row_in_tile = (rg < 0 ? 0 : rg) * 32 + l32;
   const int grow = rtile * C::RPT + row_in_tile;
-  int node = -1, slot = 0, g = 0;
-  if (rg >= 0 && grow < R) {
-    slot = grow / p.G;
-    g = grow % p.G;
+  const bool row_exists = rg >= 0 && grow < R;  // a query slot of q (its node may not exist)
+  const int slot = row_exists ? grow / p.G : 0;
+  const int g = row_exists ? grow % p.G : 0;
+
+  // Q^T operand (B side of S^T = K . Q^T): lane holds row l32, chunk 2*ks + lhi.
+  bf16x8 qreg[C::KS];
+  const uint16_t* Q = static_cast<const uint16_t*>(p.q);
+  const size_t qrow = ((static_cast<size_t>(b) * p.n_q + slot) * p.Hq + hkv * p.G + g) * D;
+
+  // A split of a contiguous cache starts at t_begin whatever the sequence's
+  // length, and its first two tiles lie inside the allocation when
+  // t_begin + 64 <= T_cap: their K/V and the tile's query rows are loaded
+  // before the lengths are known, so that the ring's first memory latency
+  // overlaps the lengths' load and the mask set-up.  (Every return below
+  // waits for these loads first: the LDS they land in must not be handed to
+  // another work group while they are in flight.)
+  const bool spec = !kRope && p.block_table == nullptr && t_begin + 2 * kTile <= p.T_cap;
+  if (spec) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int q = 0; q < C::INST_PER_WAVE; ++q) {
+        const int r0 = (wave * C::INST_PER_WAVE + q) * C::ROWS_PER_INST;
+        const int r = r0 + lane / C::CH;
+        const int c = (lane % C::CH) ^ swz<D>(r);
+        const size_t off = (static_cast<size_t>(b) * p.T_cap + t_begin + j * kTile + r) * pos_stride +
+                           static_cast<size_t>(hkv) * C::ROW + c * 16;
+        const uint32_t lk = __builtin_amdgcn_readfirstlane(ring_base + j * C::STAGE + r0 * C::ROW);
+        dma16(Kg + off, lk);
+        dma16(Vg + off, lk + C::HALF);
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (row_exists) v = *reinterpret_cast<const u32x4*>(Q + qrow + (2 * ks + lhi) * 8);
+      qreg[ks] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  SeqBounds sb;
+  if (!seq_bounds(p.prefix_len, p.n_nodes, b, p.n_max, p.T_cap, sb)) {
+    if (spec) wait_vmcnt<0>();
+    return;
+  }
+  const int nsplit = (sb.T + p.chunk - 1) / p.chunk;
+  if (split >= nsplit) {
+    if (spec) wait_vmcnt<0>();
+    return;
+  }
+  const int t_end = min(sb.T, t_begin + p.chunk);
+
+  int node = -1;
+  if (row_exists) {
     node = p.expand ? sb.n - p.n_q + slot : slot;
     if (node < 0 || node >= sb.n) node = -1;
   }
-  if (!__syncthreads_or(node >= 0)) return;
+  if (!__syncthreads_or(node >= 0)) {
+    if (spec) wait_vmcnt<0>();
+    return;
+  }
 
   // With RoPE the ring streams the prefix part of the split; the tree part
   // follows it (staged, not streamed).
@@ -92,10 +143,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
   int vis_end = t_ring_end;  // the masked path's end of visible positions
   const bool has_tree = t_end > sb.P;
 
-  // ---- setup: ancestor masks (in the ring's space), paged block ids ------------
+  // ---- setup: ancestor masks (in ring slots 2-3, which no load has
+  // reached yet), paged block ids ------------
+  static_assert(C::SETUP <= 2 * C::STAGE, "the set-up tables fit in ring slots 2 and 3");
   if constexpr (!kRope) {
-    auto sAnc = reinterpret_cast<uint64_t(*)[kMaskWords]>(sRing);
-    int* sJump = reinterpret_cast<int*>(sRing + kMaxNodes * kMaskWords * 8);
+    auto sAnc = reinterpret_cast<uint64_t(*)[kMaskWords]>(sRing + 2 * C::STAGE);
+    int* sJump = reinterpret_cast<int*>(sRing + 2 * C::STAGE + kMaxNodes * kMaskWords * 8);
     if (has_tree) build_ancestor_masks(p.parent + static_cast<size_t>(b) * p.n_max, sb.n, sAnc, sJump);
     if (p.block_table != nullptr) {
       const int blk0 = t_begin / p.block_size;
@@ -114,13 +167,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
     __syncthreads();  // the ring may now overwrite the ancestor table
   }
 
-  // Q^T operand (B side of S^T = K . Q^T): lane holds row l32, chunk 2*ks + lhi.
-  // Loaded once the first ring stages are in flight (below), so that both
-  // latencies overlap.
-  bf16x8 qreg[C::KS];
+  // The queries, loaded once the first ring stages are in flight (below), so
+  // that both latencies overlap.
   auto load_q = [&]() {
-    const uint16_t* Q = static_cast<const uint16_t*>(p.q);
-    const size_t qrow = ((static_cast<size_t>(b) * p.n_q + slot) * p.Hq + hkv * p.G + g) * D;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       u32x4 v = {0u, 0u, 0u, 0u};
@@ -134,9 +183,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
   };
 
   // ---- ring of stages ----------------------------------------------------
-  const uint8_t* Kg = static_cast<const uint8_t*>(p.k);
-  const uint8_t* Vg = static_cast<const uint8_t*>(p.v);
-  const uint32_t ring_base = static_cast<uint32_t>(reinterpret_cast<size_t>((lds_u8*)sRing));
   const int ntiles = max(0, (t_ring_end - t_begin + kTile - 1) / kTile);
   const int blk0 = (!kRope && p.block_table != nullptr) ? t_begin / p.block_size : 0;
 
@@ -156,7 +202,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
   // logical chunk pc ^ swz(r).  In the contiguous layout the byte offset of the
   // next stage to issue just advances by one tile of positions per stage.
   const bool contiguous = kRope || p.block_table == nullptr;
-  const size_t pos_stride = static_cast<size_t>(p.Hkv) * C::ROW;  // contiguous: bytes per position
   size_t dma_off[C::INST_PER_WAVE];
 #pragma unroll
   for (int q = 0; q < C::INST_PER_WAVE; ++q) {
@@ -300,8 +345,28 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
 
   // Prologue: stages 0 .. S-2 and the queries in flight, tile 0's scores started.
   if constexpr (!kRope) {
-    for (int j = 0; j < S - 1 && j < ntiles; ++j) issue_stage(j, j);
-    load_q();
+    static_assert(S == 4, "the early start covers stages 0 and 1 of four");
+    if (spec) {
+      if (t_begin + 2 * kTile > t_ring_end) {
+        // the early tiles ran past the split's end (rows there may hold
+        // anything): load them again, clamped to the split
+        wait_vmcnt<0>();
+        for (int j = 0; j < 2 && j < ntiles; ++j) issue_stage(j, j);
+      } else {
+#pragma unroll
+        for (int q = 0; q < C::INST_PER_WAVE; ++q) dma_off[q] += 2 * kTile * pos_stride;
+      }
+      // the early query loads have landed; rows without a node take zeros
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      if (node < 0) {
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) qreg[ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+      }
+      if (2 < ntiles) issue_stage(2, 2);
+    } else {
+      for (int j = 0; j < S - 1 && j < ntiles; ++j) issue_stage(j, j);
+      load_q();
+    }
   } else {
     // Stages 0 .. S-3 go out first; ring slots S-2 and S-1 hold the set-up.
     for (int j = 0; j < S - 2 && j < ntiles; ++j) issue_stage(j, j);
@@ -336,8 +401,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
     // queries: each lane holds chunks 2ks + lhi; chunk c pairs with c + D/16
     // (channels j and j + d/2), which is qreg[ks + KS/2] of the same lane
     {
-      const uint16_t* Q = static_cast<const uint16_t*>(p.q);
-      const size_t qrow = ((static_cast<size_t>(b) * p.n_q + slot) * p.Hq + hkv * p.G + g) * D;
       u32x4 raw[C::KS];
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
