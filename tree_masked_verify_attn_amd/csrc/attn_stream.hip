@@ -441,17 +441,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
   // Iteration j: tile j+1 arrives and its scores start on the matrix cores,
   // then tile j's softmax and P.V run.  Tiles below lim = min(P, t_end) need no
   // mask; the dense part is unrolled by the ring depth so that every slot
-  // offset is a constant.
+  // offset is a constant.  Its tiles go in pairs whose scores live in two
+  // alternating registers (s_cur, s_odd): with one "next scores" value copied
+  // into s_cur every tile, the compiler emitted eight 64-bit moves per tile.
+  static_assert(S % 2 == 0, "the dense loop takes tiles in pairs");
   const int n_clean = max(0, min(ntiles, (lim - t_begin) / kTile));
   int j = 0;
   for (; j + S <= n_clean && j + S < ntiles; j += S) {
 #pragma unroll
-    for (int u = 0; u < S; ++u) {
+    for (int u = 0; u < S; u += 2) {
+      f32x16 s_odd;
       arrive(j + u + 1, (u + 1) % S);
       if (rg >= 0) {
-        const f32x16 s_next = qk((u + 1) % S);
+        s_odd = qk((u + 1) % S);
         softmax_pv(s_cur, t_begin + (j + u) * kTile, u, std::false_type{});
-        s_cur = s_next;
+      }
+      arrive(j + u + 2, (u + 2) % S);
+      if (rg >= 0) {
+        s_cur = qk((u + 2) % S);
+        softmax_pv(s_odd, t_begin + (j + u + 1) * kTile, u + 1, std::false_type{});
       }
     }
   }
