@@ -237,6 +237,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[mb][r] = 0.f;
   float m_ref = -INFINITY;
+  float m_hi = -INFINITY;  // the largest tile maximum seen (log2 units)
   float l_sum = 0.f;
   const float cs = p.scale_log2;
   const int lim = min(sb.P, t_ring_end);
@@ -269,9 +270,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
     v_base_p = L + 64 * x;
     v_base_m = L - 64 * x;
   }
-  // Mask (tiles that reach the tree cache or the split's end), online softmax
-  // and O^T += V^T . P^T for the tile of positions tb.. held in ring `slot`.
-  // Lane l holds positions tb + 8*(r/4) + 4*lhi + r%4 of row l32.
+  // Mask (tiles that reach the tree cache or the split's end), online
+  // softmax and O^T += V^T . P^T for the tile of positions tb.. held in ring
+  // `slot`.  Lane l holds positions tb + 8*(r/4) + 4*lhi + r%4 of row l32.
+  // No branch: the exponentials take as reference m_use = max(m_ref, tile
+  // maximum - kRescaleMax) (the tile's own maximum while the row has seen
+  // nothing), so every p stays below 2^kRescaleMax, and the mask, the
+  // maximum, the exponentials and P.V form one block with the next tile's
+  // QK^T MFMAs, which the compiler interleaves.  The running maximum of the
+  // tiles' maxima (m_hi) is folded into the state by settle(), called after
+  // every tile: a maximum more than kRescaleSlack above m_ref rescales the
+  // state to it, so that at every tile's start the state's p are at most
+  // 2^kRescaleSlack.  When m_use passes m_ref (a jump of more than
+  // kRescaleMax), the state is left as it is: next to this tile's largest p
+  // (2^kRescaleMax) it weighs below 2^-(kRescaleMax - kRescaleSlack - 20) for
+  // up to 2^20 positions, far below fp32 resolution, scaled down or not.
   auto softmax_pv = [&](f32x16 Sc, int tb, int slot, auto masked_tag) {
     constexpr bool kMasked = decltype(masked_tag)::value;
     const uint8_t* sV = sRing + slot * C::STAGE + C::HALF;
@@ -290,28 +303,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
     float mx = Sc[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, Sc[r]);
-    mx = fmaxf(mx, lane_swap32(mx)) * cs;
-    const bool bump = mx > m_ref + kRescaleSlack;
-    if (__builtin_amdgcn_ballot_w64(bump) != 0ull) {
-      const float m_new = bump ? mx : m_ref;
-      const float alpha = (m_ref == -INFINITY) ? 0.f : exp2f(m_ref - m_new);
-      l_sum *= alpha;
-#pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[mb][r] *= alpha;
-      m_ref = m_new;
-    }
-    const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+    mx = fmaxf(mx, lane_swap32(mx)) * cs;  // the tile's row maximum (log2 units)
+    float m_use = m_ref == -INFINITY ? mx : fmaxf(m_ref, mx - kRescaleMax);
+    m_use = m_use == -INFINITY ? 0.f : m_use;  // nothing visible yet: every p is 0
     float rs = 0.f;
     bf16x8 pk[2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float pr = __builtin_amdgcn_exp2f(fmaf(Sc[r], cs, -m_use));  // v_exp_f32; args <= 8
+      const float pr = __builtin_amdgcn_exp2f(fmaf(Sc[r], cs, -m_use));  // v_exp_f32; args <= 64
       rs += pr;
       pk[r >> 3][r & 7] = static_cast<__bf16>(pr);
     }
     l_sum += rs + lane_swap32(rs);
+    m_ref = m_ref == -INFINITY ? mx : m_use;  // the state's reference from here on
+    m_hi = fmaxf(m_hi, mx);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
@@ -329,6 +334,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
         acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pk[kk],
                                                           acc[mb], 0, 0, 0);
       }
+    }
+  };
+  // After each tile (a rarely taken, wave-uniform branch, which measured
+  // cheapest there): fold m_hi into the state.  m_ref is finite whenever
+  // m_hi passes it.
+  auto settle = [&]() {
+    const bool bump = m_hi > m_ref + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(bump) != 0ull) {
+      const float alpha = bump ? exp2f(m_ref - m_hi) : 1.f;
+      l_sum *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mb][r] *= alpha;
+      m_ref = bump ? m_hi : m_ref;
     }
   };
   // Makes tile j visible to every wave: wait until stage j has landed (at most
@@ -455,11 +475,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
       if (rg >= 0) {
         s_odd = qk((u + 1) % S);
         softmax_pv(s_cur, t_begin + (j + u) * kTile, u, std::false_type{});
+        settle();
       }
       arrive(j + u + 2, (u + 2) % S);
       if (rg >= 0) {
         s_cur = qk((u + 2) % S);
         softmax_pv(s_odd, t_begin + (j + u + 1) * kTile, u + 1, std::false_type{});
+        settle();
       }
     }
   }
@@ -479,6 +501,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
             softmax_pv(s_cur, t_begin + jj * kTile, u, std::false_type{});
           else
             softmax_pv(s_cur, t_begin + jj * kTile, u, std::true_type{});
+          settle();
           s_cur = s_next;
         }
       }
@@ -567,7 +590,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
         *reinterpret_cast<u32x4*>(sV + lds_off<D>(r, c)) = a;
       }
       __syncthreads();
-      if (rg >= 0) softmax_pv(qk(0), c0, 0, std::true_type{});
+      if (rg >= 0) {
+        softmax_pv(qk(0), c0, 0, std::true_type{});
+        settle();
+      }
       __syncthreads();  // before the next group of positions overwrites slot 0
     }
   }

@@ -17,7 +17,8 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 constexpr int kThreads = 256;
 constexpr int kTile = 32;             // KV positions per ring stage
-constexpr float kRescaleSlack = 8.f;  // log2 units
+constexpr float kRescaleSlack = 8.f;  // log2 units: a larger new maximum rescales the state
+constexpr float kRescaleMax = 64.f;   // log2 units: p stay below 2^64; a larger jump outweighs the state
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr int kMaxSplitBlocks = 512;  // paged: block ids of one split cached in LDS
 
