@@ -9,9 +9,11 @@
 // the order by score is the order by logit, so:
 //
 //   1. rows: one 1024-thread work group per (row, sequence) reads the row
-//      once and keeps, at the same time, each thread's online (max, sum of
-//      exp) and its best allowed logit (a row's children are marked in an LDS
-//      bitmap).  The w-th best of the threads' best logits is a threshold no
+//      once; each thread takes its maximum, then one sum of exponentials
+//      against it, and its best allowed logit: the first occurrence of its
+//      maximum unless a child of the row's node holds that token (then a full
+//      scan; the children are marked in an LDS bitmap).  (Rows longer than
+//      one load batch keep an online maximum and sum instead.)  The w-th best of the threads' best logits is a threshold no
 //      worse than the row's w-th best allowed logit, and only the (at most w)
 //      threads whose best reaches it can hold logits that reach it; those
 //      threads put such logits in LDS, where each is ranked by counting the
@@ -264,21 +266,13 @@ __global__ __launch_bounds__(kThreads) void topw_rows_kernel(const void* logits,
     for (int e = 1; e < kPer; ++e) vmax = fmaxf(vmax, value(x, e));
     return vmax;
   };
-  for (int base = 0; base < nunits; base += step) {
-    if (base > 0) load_batch(base);
+  // The thread's best allowed logit over its units: ties keep the earlier
+  // token (a thread's tokens rise with u and e).
+  auto best_allowed = [&](int base) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int j = base + u * kThreads + tid;
       if (j >= nunits) break;
-      const float vmax = unit_max(v[u]);
-      umax[u] = vmax;
-      const float mn = fmaxf(m, vmax * kLog2e);
-      const float msub = mn == -INFINITY ? 0.f : mn;
-      float add = 0.f;
-#pragma unroll
-      for (int e = 0; e < kPer; ++e) add += __builtin_amdgcn_exp2f(value(v[u], e) * kLog2e - msub);
-      s = s * __builtin_amdgcn_exp2f(m - msub) + add;
-      m = mn;
       const uint32_t tk = taken_bits(j);
 #pragma unroll
       for (int e = 0; e < kPer; ++e) {
@@ -288,6 +282,61 @@ __global__ __launch_bounds__(kThreads) void topw_rows_kernel(const void* logits,
         kv = better ? x : kv;
         kt = better ? j * kPer + e : kt;
       }
+    }
+  };
+  if (nunits <= step) {
+    // One batch holds the thread's whole share of the row: its maximum
+    // first, then one sum of exponentials against it, and the best allowed
+    // logit is the first occurrence of that maximum unless a child of p
+    // took it (then the full scan).
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (u * kThreads + tid >= nunits) break;
+      umax[u] = unit_max(v[u]);
+      tmax = fmaxf(tmax, umax[u]);
+    }
+    m = tmax * kLog2e;
+    const float msub = m == -INFINITY ? 0.f : m;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (u * kThreads + tid >= nunits) break;
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) s += __builtin_amdgcn_exp2f(value(v[u], e) * kLog2e - msub);
+    }
+    int first = kNone;  // the first token holding tmax
+#pragma unroll
+    for (int u = kUnroll - 1; u >= 0; --u) {
+      if (u * kThreads + tid < nunits && umax[u] == tmax) {
+#pragma unroll
+        for (int e = kPer - 1; e >= 0; --e)
+          first = value(v[u], e) == tmax ? (u * kThreads + tid) * kPer + e : first;
+      }
+    }
+    if (first != kNone && ((taken_bits(first / kPer) >> (first % kPer)) & 1u) == 0u) {
+      kv = tmax;
+      kt = first;
+    } else {
+      best_allowed(0);
+    }
+  } else {
+    for (int base = 0; base < nunits; base += step) {
+      if (base > 0) load_batch(base);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int j = base + u * kThreads + tid;
+        if (j >= nunits) break;
+        const float vmax = unit_max(v[u]);
+        umax[u] = vmax;
+        const float mn = fmaxf(m, vmax * kLog2e);
+        const float msub = mn == -INFINITY ? 0.f : mn;
+        float add = 0.f;
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) add += __builtin_amdgcn_exp2f(value(v[u], e) * kLog2e - msub);
+        s = s * __builtin_amdgcn_exp2f(m - msub) + add;
+        m = mn;
+      }
+      best_allowed(base);
     }
   }
 
