@@ -434,10 +434,15 @@ __global__ __launch_bounds__(kThreads) void topw_select_kernel(int32_t* parent, 
   __shared__ int sCount, sSurvCount;
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
-  // Thread r holds row r's candidates (score, token), ranks 0 .. w-1.  A
+  // A thread holds one row's candidates (score, token), ranks 0 .. w-1.  A
   // candidate's index is row * w + rank: lower parent first (row = parent +
-  // 1), then the row's own order.
-  const int rr = tid <= n_max ? tid : n_max;
+  // 1), then the row's own order.  Consecutive rows sit in different waves
+  // (row = lane * kWaves + wave), so that every wave has rows and the
+  // threshold's bound (the w-th best wave maximum) exists: with rows in the
+  // first waves only, every head would be ranked exactly.
+  static_assert(kThreads > kMaxNodes, "a thread for every row (root + n_max nodes)");
+  const int row = (tid & 63) * kWaves + (tid >> 6);
+  const int rr = row <= n_max ? row : n_max;
   const size_t rbase = (static_cast<size_t>(b) * (n_max + 1) + rr) * w;
   float sc[kTopwMaxW];
   int tk[kTopwMaxW];
@@ -454,20 +459,20 @@ __global__ __launch_bounds__(kThreads) void topw_select_kernel(int32_t* parent, 
   if (take <= 0) return;  // uniform
   if (tid == 0) sCount = 0;
 
-  const bool row_ok = tid <= n && tk[0] >= 0;
-  const uint64_t head = row_ok ? make_key(sc[0], static_cast<uint32_t>(tid * w)) : 0ull;
+  const bool row_ok = row <= n && tk[0] >= 0;
+  const uint64_t head = row_ok ? make_key(sc[0], static_cast<uint32_t>(row * w)) : 0ull;
   const uint64_t tau = block_threshold(head, take, sSurv, sWmax, &sTau, &sSurvCount);
   if (head != 0 && head >= tau) {
     // the row's candidates that reach the threshold are a prefix of it
     int cnt = 0;
 #pragma unroll
     for (int k = 0; k < kTopwMaxW; ++k)
-      cnt += (k < w && tk[k] >= 0 && make_key(sc[k], tid * w + k) >= tau) ? 1 : 0;
+      cnt += (k < w && tk[k] >= 0 && make_key(sc[k], row * w + k) >= tau) ? 1 : 0;
     int slot = atomicAdd(&sCount, cnt);
 #pragma unroll
     for (int k = 0; k < kTopwMaxW; ++k) {
       if (k < cnt) {
-        sCand[slot + k] = make_key(sc[k], tid * w + k);
+        sCand[slot + k] = make_key(sc[k], row * w + k);
         sCandT[slot + k] = tk[k];
       }
     }
