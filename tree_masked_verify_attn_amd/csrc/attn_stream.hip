@@ -362,6 +362,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
     raw_barrier();
     if (j >= 1 && j + S - 2 < ntiles) issue_stage(j + S - 2, (slot + S - 2) % S);
   };
+  // arrive() inside the dense loop (1 <= j, j + 3 < ntiles): exactly S - 3
+  // stages after j are in flight and stage j + S - 2 exists, so the wait and
+  // the issue need no run-time cases.
+  auto arrive_dense = [&](int j, int slot) {
+    wait_vmcnt<(S - 3) * C::NL>();
+    raw_barrier();
+    issue_stage(j + S - 2, (slot + S - 2) % S);
+  };
 
   // Prologue: stages 0 .. S-2 and the queries in flight, tile 0's scores started.
   if constexpr (!kRope) {
@@ -467,17 +475,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
   static_assert(S % 2 == 0, "the dense loop takes tiles in pairs");
   const int n_clean = max(0, min(ntiles, (lim - t_begin) / kTile));
   int j = 0;
-  for (; j + S <= n_clean && j + S < ntiles; j += S) {
+  for (; j + S <= n_clean && j + S + 3 < ntiles; j += S) {  // arrive_dense's range
 #pragma unroll
     for (int u = 0; u < S; u += 2) {
       f32x16 s_odd;
-      arrive(j + u + 1, (u + 1) % S);
+      arrive_dense(j + u + 1, (u + 1) % S);
       if (rg >= 0) {
         s_odd = qk((u + 1) % S);
         softmax_pv(s_cur, t_begin + (j + u) * kTile, u, std::false_type{});
         settle();
       }
-      arrive(j + u + 2, (u + 2) % S);
+      arrive_dense(j + u + 2, (u + 2) % S);
       if (rg >= 0) {
         s_cur = qk((u + 2) % S);
         softmax_pv(s_odd, t_begin + (j + u + 1) * kTile, u + 1, std::false_type{});
