@@ -303,7 +303,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
     float mx = Sc[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, Sc[r]);
-    mx = fmaxf(mx, lane_swap32(mx)) * cs;  // the tile's row maximum (log2 units)
+    mx = halves_max(mx) * cs;  // the tile's row maximum (log2 units)
     float m_use = m_ref == -INFINITY ? mx : fmaxf(m_ref, mx - kRescaleMax);
     m_use = m_use == -INFINITY ? 0.f : m_use;  // nothing visible yet: every p is 0
     float rs = 0.f;
@@ -314,7 +314,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
       rs += pr;
       pk[r >> 3][r & 7] = static_cast<__bf16>(pr);
     }
-    l_sum += rs + lane_swap32(rs);
+    l_sum += halves_sum(rs);
     m_ref = m_ref == -INFINITY ? mx : m_use;  // the state's reference from here on
     m_hi = fmaxf(m_hi, mx);
 #pragma unroll

@@ -537,7 +537,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_units_kernel(AttnParams p) {
       float mx = Sc[0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) mx = fmaxf(mx, Sc[r]);
-      mx = fmaxf(mx, lane_swap32(mx)) * cs;
+      mx = halves_max(mx) * cs;
       const bool bump = mx > m_ref + kRescaleSlack;
       if (__builtin_amdgcn_ballot_w64(bump) != 0ull) {
         const float m_new = bump ? mx : m_ref;
@@ -558,7 +558,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_units_kernel(AttnParams p) {
         rs += pr;
         pk[r >> 3][r & 7] = static_cast<__bf16>(pr);
       }
-      l_sum += rs + lane_swap32(rs);
+      l_sum += halves_sum(rs);
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll

@@ -32,10 +32,18 @@ __device__ __forceinline__ int lds_off(int t, int chunk) {  // bytes within a K 
   return t * (D * 2) + ((chunk ^ swz<D>(t)) << 4);
 }
 
-__device__ __forceinline__ float lane_swap32(float x) {
+// x combined with the value of the lane 32 apart, the same in both lanes:
+// v_permlane32_swap of x with itself leaves the lower half's values in both
+// halves of one result and the upper half's in both halves of the other.
+__device__ __forceinline__ float halves_max(float x) {
   const uint32_t u = __float_as_uint(x);
   const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return __uint_as_float((threadIdx.x & 63) < 32 ? r[1] : r[0]);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // 64 lanes x 16 bytes from `g` (per lane) into LDS [lds_base, lds_base + 1 KiB).
