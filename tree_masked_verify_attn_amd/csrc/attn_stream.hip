@@ -62,7 +62,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
   const int hkv = bh % p.Hkv;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: load bases in SGPRs
   const int lhi = lane >> 5;
   const int l32 = lane & 31;
   const int t_begin = split * p.chunk;
@@ -210,24 +210,32 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
     dma_off[q] = (static_cast<size_t>(b) * p.T_cap + t_begin + r) * pos_stride +
                  static_cast<size_t>(hkv) * C::ROW + c * 16;
   }
-  // Issues stage j (the stages are issued in order) into ring slot `slot`.
-  auto issue_stage = [&](int j, int slot) {
+  // Issues stage j (the stages are issued in order) into ring slot `slot`;
+  // whole_tag true: the stage is known to be a whole tile inside the split.
+  auto issue_stage = [&](int j, int slot, auto whole_tag) {
     const int tb = t_begin + j * kTile;
     const uint32_t sbase = ring_base + slot * C::STAGE;
-    const bool fast = contiguous && tb + kTile <= t_ring_end;
+    const bool fast = contiguous && (decltype(whole_tag)::value || tb + kTile <= t_ring_end);
+    if (fast) {
 #pragma unroll
-    for (int q = 0; q < C::INST_PER_WAVE; ++q) {
-      const int r0 = (wave * C::INST_PER_WAVE + q) * C::ROWS_PER_INST;
-      size_t off = dma_off[q];
-      if (!fast) {
+      for (int q = 0; q < C::INST_PER_WAVE; ++q) {
+        const uint32_t lk = sbase + (wave * C::INST_PER_WAVE + q) * C::ROWS_PER_INST * C::ROW;
+        dma16(Kg + dma_off[q], lk);
+        dma16(Vg + dma_off[q], lk + C::HALF);
+        dma_off[q] += kTile * pos_stride;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < C::INST_PER_WAVE; ++q) {
+        const int r0 = (wave * C::INST_PER_WAVE + q) * C::ROWS_PER_INST;
         const int r = r0 + lane / C::CH;
         const int c = (lane % C::CH) ^ swz<D>(r);
-        off = row_bytes_off(tb + r) + c * 16;
+        const size_t off = row_bytes_off(tb + r) + c * 16;
+        const uint32_t lk = sbase + r0 * C::ROW;
+        dma16(Kg + off, lk);
+        dma16(Vg + off, lk + C::HALF);
+        dma_off[q] += kTile * pos_stride;
       }
-      dma_off[q] += kTile * pos_stride;
-      const uint32_t lk = __builtin_amdgcn_readfirstlane(sbase + r0 * C::ROW);
-      dma16(Kg + off, lk);
-      dma16(Vg + off, lk + C::HALF);
     }
   };
 
@@ -360,7 +368,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
     const int issued_last = min(j == 0 ? S - 2 : j + S - 3, ntiles - 1);
     wait_stage<S - 2, C::NL>(issued_last - j);
     raw_barrier();
-    if (j >= 1 && j + S - 2 < ntiles) issue_stage(j + S - 2, (slot + S - 2) % S);
+    if (j >= 1 && j + S - 2 < ntiles) issue_stage(j + S - 2, (slot + S - 2) % S, std::false_type{});
   };
   // arrive() inside the dense loop (1 <= j, j + 3 < ntiles): exactly S - 3
   // stages after j are in flight and stage j + S - 2 exists, so the wait and
@@ -368,7 +376,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
   auto arrive_dense = [&](int j, int slot) {
     wait_vmcnt<(S - 3) * C::NL>();
     raw_barrier();
-    issue_stage(j + S - 2, (slot + S - 2) % S);
+    issue_stage(j + S - 2, (slot + S - 2) % S, std::true_type{});
   };
 
   // Prologue: stages 0 .. S-2 and the queries in flight, tile 0's scores started.
@@ -379,7 +387,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
         // the early tiles ran past the split's end (rows there may hold
         // anything): load them again, clamped to the split
         wait_vmcnt<0>();
-        for (int j = 0; j < 2 && j < ntiles; ++j) issue_stage(j, j);
+        for (int j = 0; j < 2 && j < ntiles; ++j) issue_stage(j, j, std::false_type{});
       } else {
 #pragma unroll
         for (int q = 0; q < C::INST_PER_WAVE; ++q) dma_off[q] += 2 * kTile * pos_stride;
@@ -390,14 +398,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) qreg[ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
       }
-      if (2 < ntiles) issue_stage(2, 2);
+      if (2 < ntiles) issue_stage(2, 2, std::false_type{});
     } else {
-      for (int j = 0; j < S - 1 && j < ntiles; ++j) issue_stage(j, j);
+      for (int j = 0; j < S - 1 && j < ntiles; ++j) issue_stage(j, j, std::false_type{});
       load_q();
     }
   } else {
     // Stages 0 .. S-3 go out first; ring slots S-2 and S-1 hold the set-up.
-    for (int j = 0; j < S - 2 && j < ntiles; ++j) issue_stage(j, j);
+    for (int j = 0; j < S - 2 && j < ntiles; ++j) issue_stage(j, j, std::false_type{});
     uint8_t* setup = sRing + (S - 2) * C::STAGE;
     auto sAnc = reinterpret_cast<uint64_t(*)[kMaskWords]>(setup);
     int* sJump = reinterpret_cast<int*>(setup + kMaxNodes * kMaskWords * 8);
@@ -462,7 +470,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the query loads (and the first stages)
     }
     __syncthreads();  // the table is done with: slot S-2 takes its stage
-    if (S - 2 < ntiles) issue_stage(S - 2, S - 2);
+    if (S - 2 < ntiles) issue_stage(S - 2, S - 2, std::false_type{});
   }
   if (ntiles > 0) arrive(0, 0);
   f32x16 s_cur = (rg >= 0 && ntiles > 0) ? qk(0) : f32x16{};
