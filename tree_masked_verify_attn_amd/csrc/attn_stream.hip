@@ -71,7 +71,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
   const uint32_t ring_base = static_cast<uint32_t>(reinterpret_cast<size_t>((lds_u8*)sRing));
   const size_t pos_stride = static_cast<size_t>(p.Hkv) * C::ROW;  // contiguous: bytes per position
 
-  const int rg = wave < NRG ? wave : -1;  // computing waves own one 32-row group each
+  // computing waves own one 32-row group each (with NRG = 4, every wave)
+  constexpr bool kAllCompute = NRG == kThreads / 64;
+  const int rg = (kAllCompute || wave < NRG) ? wave : -1;
   const int R = p.n_q * p.G;
   const int row_in_tile = (rg < 0 ? 0 : rg) * 32 + l32;
   const int grow = rtile * C::RPT + row_in_tile;
@@ -488,13 +490,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
     for (int u = 0; u < S; u += 2) {
       f32x16 s_odd;
       arrive_dense(j + u + 1, (u + 1) % S);
-      if (rg >= 0) {
+      if (kAllCompute || rg >= 0) {
         s_odd = qk((u + 1) % S);
         softmax_pv(s_cur, t_begin + (j + u) * kTile, u, std::false_type{});
         settle();
       }
       arrive_dense(j + u + 2, (u + 2) % S);
-      if (rg >= 0) {
+      if (kAllCompute || rg >= 0) {
         s_cur = qk((u + 2) % S);
         softmax_pv(s_odd, t_begin + (j + u + 1) * kTile, u + 1, std::false_type{});
         settle();
@@ -510,7 +512,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_stream_kernel(AttnParams p) 
       if (jj < ntiles) {
         const bool more = jj + 1 < ntiles;
         if (more) arrive(jj + 1, (u + 1) % S);
-        if (rg >= 0) {
+        if (kAllCompute || rg >= 0) {
           f32x16 s_next = {};
           if (more) s_next = qk((u + 1) % S);
           if (jj < n_clean)
