@@ -101,8 +101,10 @@ typedef struct {
  * sizes, enough for the plan of a contiguous and of a paged cache alike.
  * n_q is n_max for verify and w for expand.  The workspace holds the split-KV
  * partial results (per split or work-group range and query row: running
- * maximum, sum and unnormalised output) that a second, combining launch of
- * the same call reads, and for kernel 4 its table of stream starts; its
+ * maximum, sum and unnormalised output, the output in fp32 for the generic
+ * kernel and in fp16 under a per-row power-of-two scale for the bf16 MFMA
+ * kernels) that a second, combining launch of the same call reads, and for
+ * kernel 4 its table of stream starts; its
  * contents need no initialisation and are meaningless between calls.  Calls
  * that overlap in time must not share a workspace.  Returns 0 when the plans
  * need none (kernels 1-3 without a split; ws may then be NULL), or

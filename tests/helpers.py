@@ -143,8 +143,12 @@ def assert_counting_exact(O, L, O_x, L_x, what=""):
     fp32 sums are exact integers; LSE = (0 + log2 l) * ln 2 is within a few
     float32 ulp of ln l (hardware log2 ~1 ulp, the product 0.5 ulp); the
     output is count * (1/l) (two fp32 roundings) rounded once to bf16
-    (half a bf16 ulp, at most 2^-8 relative).  Zero channels must be exactly
-    zero and the identity channel exactly its integer code."""
+    (half a bf16 ulp, at most 2^-8 relative).  A split row's partial sums
+    are kept in fp16 for the combine (at most 2^-11 relative; the MFMA
+    kernels), so the bar is 2^-8 + 2^-11 plus 2^-18 for the cross terms and
+    the fp32 roundings.  Zero channels must be exactly zero and the identity
+    channel exactly its integer code (within 2^-11 of an integer that bf16
+    holds exactly, the output rounds to it)."""
     rows = ~np.isnan(O_x[..., 0, 0])
     Lr = np.transpose(L, (0, 2, 1))[rows]            # [rows][Hq]
     Lx = np.transpose(L_x, (0, 2, 1))[rows]
@@ -155,7 +159,7 @@ def assert_counting_exact(O, L, O_x, L_x, what=""):
         raise AssertionError(f"{what}: LSE off by {errL[i]:.1f} fp32 ulp at row {i} "
                              f"(got {Lr[i]!r}, expected {Lx[i]!r})")
     Og, Ox = O[rows], O_x[rows]
-    bound = (2.0 ** -8 + 2.0 ** -20) * np.abs(Ox)
+    bound = (2.0 ** -8 + 2.0 ** -11 + 2.0 ** -18) * np.abs(Ox)
     bad = np.abs(Og - Ox) > bound
     if bad.any():
         i = np.unravel_index(np.argmax(np.abs(Og - Ox) - bound), Og.shape)

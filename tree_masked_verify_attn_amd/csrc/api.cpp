@@ -304,18 +304,22 @@ int run_attention(const void* q, ta_kv kv, const int32_t* prefix_len, const int3
   p.n_split = pl.n_split;
   p.rows_per_tile = pl.rows_per_tile;
   p.n_row_tiles = pl.n_row_tiles;
+  // The MFMA kernels leave half-precision partial states (d fp16 values and a
+  // 16-byte record per row) in the space sized for fp32 ones (d + 2 floats).
+  p.ws_f16 = pl.kernel >= 2 ? 1 : 0;
+  const size_t o_bytes = p.ws_f16 ? sizeof(uint16_t) : sizeof(float);
   if (pl.kernel == 4) {
     const size_t slots = 2 * static_cast<size_t>(pl.n_split) * pl.rows_per_tile;
     uint8_t* base = static_cast<uint8_t*>(ws);
     p.ws_o = reinterpret_cast<float*>(base);
-    p.ws_ml = reinterpret_cast<float*>(base + slots * d * sizeof(float));
+    p.ws_ml = reinterpret_cast<float*>(base + slots * d * o_bytes);
     p.ws_seq = reinterpret_cast<int32_t*>(base + slots * (d + 2) * sizeof(float));
   } else if (pl.ws_bytes > 0) {
     const int tiles = B * Hkv * pl.n_row_tiles;
     const size_t parts = static_cast<size_t>(tiles) * pl.n_split * pl.rows_per_tile;
     uint8_t* base = static_cast<uint8_t*>(ws);
     p.ws_o = reinterpret_cast<float*>(base);
-    p.ws_ml = reinterpret_cast<float*>(base + parts * d * sizeof(float));
+    p.ws_ml = reinterpret_cast<float*>(base + parts * d * o_bytes);
   }
   if (fused_rope) {
     p.rope = 1;

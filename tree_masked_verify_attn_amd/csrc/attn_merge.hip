@@ -10,8 +10,10 @@
 // The combine runs as its own launch: on gfx950 the kernel boundary makes the
 // partial results visible to every compute unit once, whereas a device-scope
 // release/acquire in each splitting work group writes back and invalidates
-// the whole L2 of its XCD every time.
-#include "ta_device.h"
+// the whole L2 of its XCD every time.  The bf16 MFMA kernels leave their
+// partial outputs in half precision (partial_f16.h), the generic kernel in
+// fp32.
+#include "partial_f16.h"
 
 namespace ta {
 namespace {
@@ -36,7 +38,7 @@ __device__ __forceinline__ void store4<uint16_t>(uint16_t* out, f32x4 v) {
 
 // grid = (sequence x KV head, row-tile x channel-group blocks); one thread
 // per (row, 4 channels) of a tile.
-template <typename T>
+template <typename T, bool F16>
 __global__ __launch_bounds__(kThreads) void merge_kernel(AttnParams p) {
   const int bh = blockIdx.x;
   const int b = bh / p.Hkv;
@@ -57,39 +59,67 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(AttnParams p) {
   // sequence's last split are discarded below.
   float ms[kBatch], ls[kBatch];
   f32x4 os[kBatch];
+  PartialF16 hs[kBatch];  // half-precision states as loaded
   auto load_batch = [&](int s0, int last) {
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
       const int sp = s0 + k < last ? s0 + k : last;
       const size_t pr = (part + sp) * p.rows_per_tile + r;
-      const float2 ml = *reinterpret_cast<const float2*>(p.ws_ml + pr * 2);
-      ms[k] = ml.x;
-      ls[k] = ml.y;
-      os[k] = *reinterpret_cast<const f32x4*>(p.ws_o + pr * p.d + 4 * dg);
+      if constexpr (F16) {
+        hs[k] = load_partial_f16(reinterpret_cast<const uint16_t*>(p.ws_o) + pr * p.d + 4 * dg,
+                                 reinterpret_cast<const PartialRec*>(p.ws_ml) + pr);
+      } else {
+        const float2 ml = *reinterpret_cast<const float2*>(p.ws_ml + pr * 2);
+        ms[k] = ml.x;
+        ls[k] = ml.y;
+        os[k] = *reinterpret_cast<const f32x4*>(p.ws_o + pr * p.d + 4 * dg);
+      }
     }
   };
   load_batch(0, p.n_split - 1);
+  // The exits below use the first batch, so that its loads stay ahead of the
+  // sequence's bounds: the compiler would otherwise sink them past the exits,
+  // and the two memory latencies would add up.
+  static_assert(kBatch == 4, "keep_first_batch names four partial states");
+  auto keep_first_batch = [&]() {
+    if constexpr (F16) {
+      asm volatile("" ::"v"(hs[0].rec), "v"(hs[1].rec), "v"(hs[2].rec), "v"(hs[3].rec));
+      asm volatile("" ::"v"(hs[0].h), "v"(hs[1].h), "v"(hs[2].h), "v"(hs[3].h));
+    } else {
+      asm volatile("" ::"v"(ms[0]), "v"(ms[1]), "v"(ms[2]), "v"(ms[3]), "v"(ls[0]), "v"(ls[1]),
+                   "v"(ls[2]), "v"(ls[3]));
+      asm volatile("" ::"v"(os[0]), "v"(os[1]), "v"(os[2]), "v"(os[3]));
+    }
+  };
   SeqBounds sb;
-  if (!seq_bounds(p.prefix_len, p.n_nodes, b, p.n_max, p.T_cap, sb)) return;
+  if (!seq_bounds(p.prefix_len, p.n_nodes, b, p.n_max, p.T_cap, sb)) return keep_first_batch();
   const int nsplit = (sb.T + p.chunk - 1) / p.chunk;
-  if (nsplit <= 1) return;  // the attention kernel wrote this sequence's results
+  if (nsplit <= 1) return keep_first_batch();  // the attention kernel wrote this sequence's results
   const int gr = rtile * p.rows_per_tile + r;
   const int R = p.n_q * p.G;
-  if (gr >= R) return;
+  if (gr >= R) return keep_first_batch();
   const int slot = gr / p.G, g = gr % p.G;
   const int node = p.expand ? sb.n - p.n_q + slot : slot;
-  if (node < 0 || node >= sb.n) return;
+  if (node < 0 || node >= sb.n) return keep_first_batch();
 
   float M = -INFINITY, L = 0.f;
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < nsplit; s0 += kBatch) {
     if (s0 > 0) load_batch(s0, nsplit - 1);
+    if constexpr (F16) {
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        ms[k] = hs[k].rec[0];
+        ls[k] = hs[k].rec[1];
+      }
+    }
 #pragma unroll
     for (int k = 0; k < kBatch; ++k)
       if (s0 + k >= nsplit) {  // not a split of this sequence (may hold stale bytes)
         ms[k] = -INFINITY;
         ls[k] = 0.f;
         os[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+        hs[k].h = f16x4{0, 0, 0, 0};
       }
     float Mb = M;
 #pragma unroll
@@ -102,7 +132,8 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(AttnParams p) {
     for (int k = 0; k < kBatch; ++k) {
       const float wgt = (ms[k] == -INFINITY) ? 0.f : exp2f(ms[k] - Mb);
       L = fmaf(ls[k], wgt, L);
-      o += os[k] * wgt;
+      if constexpr (F16) add_partial_f16(o, hs[k], wgt);
+      else o += os[k] * wgt;
     }
     M = Mb;
   }
@@ -119,8 +150,9 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(AttnParams p) {
 hipError_t launch_attn_merge(const AttnParams& p, int dtype, hipStream_t s) {
   const long long items = static_cast<long long>(p.n_row_tiles) * p.rows_per_tile * (p.d / 4);
   const dim3 grid(p.B * p.Hkv, static_cast<unsigned>((items + kThreads - 1) / kThreads));
-  if (dtype == TA_F32) return launch(merge_kernel<float>, grid, dim3(kThreads), s, p);
-  return launch(merge_kernel<uint16_t>, grid, dim3(kThreads), s, p);
+  if (dtype == TA_F32) return launch(merge_kernel<float, false>, grid, dim3(kThreads), s, p);
+  if (p.ws_f16) return launch(merge_kernel<uint16_t, true>, grid, dim3(kThreads), s, p);
+  return launch(merge_kernel<uint16_t, false>, grid, dim3(kThreads), s, p);
 }
 
 }  // namespace ta

@@ -32,6 +32,7 @@
 //    prefetched into registers while the current one is consumed.
 //  * A split sequence leaves partial (max, sum, output) states in the
 //    workspace; the combine launch (attn_merge.hip) finishes it.
+#include "partial_f16.h"
 #include "ta_device.h"
 
 namespace ta {
@@ -348,20 +349,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnParams p) {
   // ---- publish the partial state for the combine launch --------------------
   const int tile_id = bh * p.n_row_tiles + rtile;
   const size_t part = static_cast<size_t>(tile_id) * p.n_split;
-  if (owner) {
-    float* po = p.ws_o + ((part + split) * C::RPT + row_in_tile) * D;
-#pragma unroll
-    for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d = 32 * mb + 8 * q4 + 4 * lhi;
-        *reinterpret_cast<f32x4*>(po + d) =
-            f32x4{acc[mb][4 * q4], acc[mb][4 * q4 + 1], acc[mb][4 * q4 + 2], acc[mb][4 * q4 + 3]};
-      }
-    if (lhi == 0) {
-      p.ws_ml[((part + split) * C::RPT + row_in_tile) * 2 + 0] = m_ref;
-      p.ws_ml[((part + split) * C::RPT + row_in_tile) * 2 + 1] = l_sum;
-    }
+  if (owner) {  // wave-uniform: every lane takes part in the row maximum
+    const size_t pr = (part + split) * C::RPT + row_in_tile;
+    const int e = partial_exp(acc);
+    store_partial_f16(acc, m_ref, l_sum, e, lhi, reinterpret_cast<uint16_t*>(p.ws_o) + pr * D,
+                      reinterpret_cast<PartialRec*>(p.ws_ml) + pr);
   }
   // the combine launch (attn_merge.hip) finishes split sequences
 }

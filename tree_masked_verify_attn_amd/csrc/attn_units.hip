@@ -24,8 +24,8 @@
 //  * A segment that covers a whole job writes the final rows.  A job cut by a
 //    range boundary leaves one partial (max, sum, output) state per group it
 //    touches, in slot 2g (the piece that starts the group's range) or 2g + 1
-//    (the piece that ends it); the combine launch (merge_units_kernel) adds
-//    them up.
+//    (the piece that ends it), in half precision (partial_f16.h); the combine
+//    launch (merge_units_kernel) adds them up.
 //  * Segments are set up in batches (at most kMaxSeg segments, a few of them
 //    reaching a tree cache, kUnitBlocks paged block ids); a group whose
 //    range needs more drains the ring and sets up the next batch, carrying
@@ -455,8 +455,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_units_kernel(AttnParams p) {
     };
     // Results of the compute-side segment, which ends here.
     auto end_segment = [&]() {
-      if (rg < 0 || node < 0) return;
+      if (rg < 0) return;  // wave-uniform
       if (from_job_start && (c_flags & kToJobEnd)) {  // the whole job: final rows
+        if (node < 0) return;
         uint16_t* Out = static_cast<uint16_t*>(p.out);
         const size_t orow = ((static_cast<size_t>(c_b) * p.n_q + slot) * p.Hq + c_hkv * p.G + gq) * D;
         const float inv = 1.f / l_sum;
@@ -477,20 +478,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_units_kernel(AttnParams p) {
         }
         return;
       }
-      const size_t ps = 2 * static_cast<size_t>(g) + (from_range_start ? 0 : 1);
-      float* po = p.ws_o + (ps * RPT + row_in_tile) * D;
-#pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int d = 32 * mb + 8 * q4 + 4 * lhi;
-          *reinterpret_cast<f32x4*>(po + d) =
-              f32x4{acc[mb][4 * q4], acc[mb][4 * q4 + 1], acc[mb][4 * q4 + 2], acc[mb][4 * q4 + 3]};
-        }
-      if (lhi == 0) {
-        p.ws_ml[(ps * RPT + row_in_tile) * 2 + 0] = m_ref;
-        p.ws_ml[(ps * RPT + row_in_tile) * 2 + 1] = l_sum;
-      }
+      // a piece of a cut job: its partial state in slot 2g or 2g + 1
+      const int e = partial_exp(acc);  // every lane of the wave
+      if (node < 0) return;
+      const size_t pr = (2 * static_cast<size_t>(g) + (from_range_start ? 0 : 1)) * RPT + row_in_tile;
+      store_partial_f16(acc, m_ref, l_sum, e, lhi, reinterpret_cast<uint16_t*>(p.ws_o) + pr * D,
+                        reinterpret_cast<PartialRec*>(p.ws_ml) + pr);
     };
 
     // S^T = K . Q^T for the tile in ring slot `sl`.
@@ -698,16 +691,19 @@ __global__ __launch_bounds__(kThreads) void merge_units_kernel(AttnParams p) {
   constexpr int kBatch = 4;
   for (int q0 = g0; q0 <= g1; q0 += kBatch) {
     float ms[kBatch], ls[kBatch];
-    f32x4 os[kBatch];
+    PartialF16 hs[kBatch];
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
+    for (int k = 0; k < kBatch; ++k) {  // the whole batch's loads first
       const int gg = q0 + k <= g1 ? q0 + k : g1;
       const size_t ps = 2 * static_cast<size_t>(gg) + ((gg == g0 && J0 != g0 * U) ? 1 : 0);
       const size_t pr = ps * RPT + r;
-      const float2 ml = *reinterpret_cast<const float2*>(p.ws_ml + pr * 2);
-      ms[k] = ml.x;
-      ls[k] = ml.y;
-      os[k] = *reinterpret_cast<const f32x4*>(p.ws_o + pr * p.d + 4 * dg);
+      hs[k] = load_partial_f16(reinterpret_cast<const uint16_t*>(p.ws_o) + pr * p.d + 4 * dg,
+                               reinterpret_cast<const PartialRec*>(p.ws_ml) + pr);
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      ms[k] = hs[k].rec[0];
+      ls[k] = hs[k].rec[1];
     }
 #pragma unroll
     for (int k = 0; k < kBatch; ++k)
@@ -723,7 +719,7 @@ __global__ __launch_bounds__(kThreads) void merge_units_kernel(AttnParams p) {
     for (int k = 0; k < kBatch; ++k) {
       const float wgt = (ms[k] == -INFINITY) ? 0.f : exp2f(ms[k] - Mb);
       Lsum = fmaf(ls[k], wgt, Lsum);
-      o += os[k] * wgt;
+      add_partial_f16(o, hs[k], wgt);
     }
     M = Mb;
   }

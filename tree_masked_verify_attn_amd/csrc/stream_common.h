@@ -3,6 +3,7 @@
 // the LDS-DMA issue and its explicit waits, and the stage geometry.
 #pragma once
 
+#include "partial_f16.h"
 #include "ta_device.h"
 
 namespace ta {

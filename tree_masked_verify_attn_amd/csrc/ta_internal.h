@@ -60,6 +60,9 @@ struct AttnParams {
   // workspace (only when n_split > 1)
   float* ws_o;          // [tiles][n_split][rows_per_tile][d] unnormalised partial outputs
   float* ws_ml;         // [tiles][n_split][rows_per_tile][2]  running max (log2) and sum
+  // ws_f16 = 1 (the bf16 MFMA kernels): ws_o holds the partial outputs in
+  // half precision and ws_ml 16-byte records instead (layout in partial_f16.h)
+  int32_t ws_f16;
   // units kernel only: n_split is its number of work groups G, ws_o / ws_ml
   // hold 2G slots of rows_per_tile rows, ws_seq the stream start of every
   // sequence and the stream's length (B + 1 entries)
