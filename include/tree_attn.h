@@ -104,7 +104,7 @@ typedef struct {
  * maximum, sum and unnormalised output, the output in fp32 for the generic
  * kernel and in fp16 under a per-row power-of-two scale for the bf16 MFMA
  * kernels) that a second, combining launch of the same call reads, and for
- * kernel 4 its table of stream starts; its
+ * kernel 4 a 16-byte record per sequence (its place in the work stream); its
  * contents need no initialisation and are meaningless between calls.  Calls
  * that overlap in time must not share a workspace.  Returns 0 when the plans
  * need none (kernels 1-3 without a split; ws may then be NULL), or

@@ -109,7 +109,7 @@ bool make_plan(int B, int n_q, int Hq, int Hkv, int d, int dtype, int T_cap, boo
     pl.n_split = groups;
     const size_t slots = 2 * static_cast<size_t>(groups) * pl.rows_per_tile;
     pl.ws_bytes = slots * d * sizeof(float) + slots * 2 * sizeof(float) +
-                  (static_cast<size_t>(B) + 1) * sizeof(int32_t);
+                  static_cast<size_t>(B) * 4 * sizeof(int32_t);
     return true;
   }
   int chunk = opts ? opts->chunk_tokens : 0;

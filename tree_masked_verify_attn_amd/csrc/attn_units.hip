@@ -69,10 +69,11 @@ struct SeqJobs {
   int rt_lo;   // first row tile with a valid row
   int rts;     // row tiles with valid rows (jobs per KV head)
 };
-__device__ __forceinline__ SeqJobs seq_jobs(const AttnParams& p, int b, int RPT) {
+// (from the raw prefix_len[b] and n_nodes[b])
+__device__ __forceinline__ SeqJobs seq_jobs_of(const AttnParams& p, int P_raw, int n_raw, int RPT) {
   SeqJobs s{0, 0, 0, 0, 0, 0};
   SeqBounds sb;
-  if (!seq_bounds(p.prefix_len, p.n_nodes, b, p.n_max, p.T_cap, sb)) return s;
+  if (!seq_bounds_of(P_raw, n_raw, p.n_max, p.T_cap, sb)) return s;
   const int R = p.n_q * p.G;
   int r_lo = 0, r_hi = R;
   if (p.expand) {
@@ -89,6 +90,9 @@ __device__ __forceinline__ SeqJobs seq_jobs(const AttnParams& p, int b, int RPT)
   s.rt_lo = r_lo / RPT;
   s.rts = (r_hi + RPT - 1) / RPT - s.rt_lo;
   return s;
+}
+__device__ __forceinline__ SeqJobs seq_jobs(const AttnParams& p, int b, int RPT) {
+  return seq_jobs_of(p, p.prefix_len[b], p.n_nodes[b], RPT);
 }
 
 template <int D, int NRG>
@@ -185,8 +189,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_units_kernel(AttnParams p) {
   };
 
   int Sh = load_stream();  // stream units (all KV heads)
-  if (g == 0) {  // the combine launch reads the stream starts
-    for (int b = tid; b <= B; b += kThreads) p.ws_seq[b] = sS[b];
+  if (g == 0) {  // the combine launch reads, per sequence, one 16-byte record
+    for (int b = tid; b < B; b += kThreads)
+      reinterpret_cast<int4*>(p.ws_seq)[b] = int4{sS[b], sS[B], sP[b], sN[b]};
   }
   const int N = Sh;
   const int U = (N + G - 1) / G;
@@ -660,10 +665,13 @@ __global__ __launch_bounds__(kThreads) void merge_units_kernel(AttnParams p) {
   const int bh = blockIdx.x;
   const int b = bh / p.Hkv;
   const int hkv = bh % p.Hkv;
-  // the stream starts load alongside the sequence's lengths
-  const int Sh = p.ws_seq[p.B];  // stream units (all KV heads)
-  const int seq0 = p.ws_seq[b];
-  const SeqJobs s = seq_jobs(p, b, RPT);
+  // One load brings the sequence's stream start, the stream's length and the
+  // bounds the attention launch took (P, n; 0, 0 for a sequence with nothing
+  // to do), instead of dependent rounds of loads.
+  const int4 rec = reinterpret_cast<const int4*>(p.ws_seq)[b];
+  const int seq0 = rec.x;
+  const int Sh = rec.y;  // stream units (all KV heads)
+  const SeqJobs s = seq_jobs_of(p, rec.z, rec.w, RPT);
   if (s.rts == 0) return;
   const int groups = p.d / 4;
   const int per_tile = RPT * groups;
@@ -708,10 +716,11 @@ __global__ __launch_bounds__(kThreads) void merge_units_kernel(AttnParams p) {
 #pragma unroll
     for (int k = 0; k < kBatch; ++k)
       if (q0 + k > g1) ms[k] = -INFINITY;
+    // (no early continue when every state is empty: all weights are then
+    // zero and the loads of the outputs stay ahead of the row records' use)
     float Mb = M;
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) Mb = fmaxf(Mb, ms[k]);
-    if (Mb == -INFINITY) continue;
     const float a = (M == -INFINITY) ? 0.f : exp2f(M - Mb);
     Lsum *= a;
     o *= a;

@@ -53,10 +53,8 @@ struct SeqBounds {
   int T;  // P + n, <= T_cap
 };
 
-__device__ __forceinline__ bool seq_bounds(const int32_t* prefix_len, const int32_t* n_nodes,
-                                           int b, int n_max, int T_cap, SeqBounds& sb) {
-  int n = n_nodes[b];
-  int P = prefix_len[b];
+// The same from the raw prefix_len[b] and n_nodes[b].
+__device__ __forceinline__ bool seq_bounds_of(int P, int n, int n_max, int T_cap, SeqBounds& sb) {
   n = n < 0 ? 0 : (n > n_max ? n_max : n);
   if (P < 0 || n == 0) return false;
   if (static_cast<long long>(P) + n > T_cap) return false;
@@ -64,6 +62,10 @@ __device__ __forceinline__ bool seq_bounds(const int32_t* prefix_len, const int3
   sb.n = n;
   sb.T = P + n;
   return true;
+}
+__device__ __forceinline__ bool seq_bounds(const int32_t* prefix_len, const int32_t* n_nodes,
+                                           int b, int n_max, int T_cap, SeqBounds& sb) {
+  return seq_bounds_of(prefix_len[b], n_nodes[b], n_max, T_cap, sb);
 }
 
 // Parent of node i with invalid entries read as -1 (child of the root).

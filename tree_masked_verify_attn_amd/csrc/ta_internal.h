@@ -64,8 +64,9 @@ struct AttnParams {
   // half precision and ws_ml 16-byte records instead (layout in partial_f16.h)
   int32_t ws_f16;
   // units kernel only: n_split is its number of work groups G, ws_o / ws_ml
-  // hold 2G slots of rows_per_tile rows, ws_seq the stream start of every
-  // sequence and the stream's length (B + 1 entries)
+  // hold 2G slots of rows_per_tile rows, ws_seq one 16-byte record per
+  // sequence (its stream start, the stream's length, and the P and n the
+  // attention launch took)
   int32_t* ws_seq;
   // RoPE on load (streaming kernel only, contiguous caches): q holds the
   // un-rotated queries, k_new / v_new [B][n_q][Hkv][d] the new nodes' keys
