@@ -86,7 +86,7 @@ def kernel_source_hash() -> str:
     csrc = os.path.join(ROOT, "tree_masked_verify_attn_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
         if f.startswith("attn_") or f in ("ta_device.h", "ta_internal.h", "stream_common.h",
-                                          "api.cpp"):
+                                          "partial_f16.h", "rope_common.h", "api.cpp"):
             h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
