@@ -134,6 +134,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_units_kernel(AttnParams p) {
   const int row_in_tile = (rg < 0 ? 0 : rg) * 32 + l32;
   const int B = p.B;
   const int bs = p.block_size;
+  // block sizes that are powers of two (16 in the usual serving layouts) split
+  // a position into (block, row) with a shift and a mask
+  const int bs_shift = (bs & (bs - 1)) == 0 ? __builtin_ctz(static_cast<unsigned>(bs)) : -1;
   const bool paged = p.block_table != nullptr;
 
   // per sequence: start of its tiles (all KV heads) in the stream
@@ -385,29 +388,48 @@ __global__ __launch_bounds__(kThreads, 2) void attn_units_kernel(AttnParams p) {
     load_i(0);
 
     // Issues stage j (the stages are issued in order) into ring slot `sl`.
+    // Every address of the stage first (a paged stage reads its block ids
+    // from LDS in one round), then the loads: the DMA's memory clobber would
+    // otherwise hold each block-id read behind the previous row's loads.
     auto issue_stage = [&](int j, int sl) {
       if (!loader) return;  // wave-uniform
       while (j >= i_j1) load_i(++ki);  // uniform; ki < nseg since j < L
       const uint32_t sbase = ring_base + sl * C::STAGE;
       const int tb = i_tb0 + j * kTile;
+      size_t off[kInst];
+      auto addresses = [&](auto pow2_tag) {
+#pragma unroll
+        for (int q = 0; q < kInst; ++q) {
+          const int r = (dma_rank * kInst + q) * C::ROWS_PER_INST + lane / C::CH;
+          const int c = (lane % C::CH) ^ swz<D>(r);
+          int tok = tb + r;
+          tok = tok < i_te ? tok : i_te - 1;
+          size_t row;
+          if (paged) {
+            int bi, in;
+            if constexpr (decltype(pow2_tag)::value) {
+              bi = tok >> bs_shift;
+              in = tok & (bs - 1);
+            } else {
+              bi = tok / bs;
+              in = tok - bi * bs;
+            }
+            const int blk = sBlk[i_blkoff + bi - i_blk0];
+            row = (static_cast<size_t>(blk) * bs + in) * p.Hkv + i_hkv;
+          } else {
+            row = (static_cast<size_t>(i_b) * p.T_cap + tok) * p.Hkv + i_hkv;
+          }
+          off[q] = row * C::ROW + c * 16;
+        }
+      };
+      if (bs_shift >= 0) addresses(std::true_type{});
+      else addresses(std::false_type{});
 #pragma unroll
       for (int q = 0; q < kInst; ++q) {
         const int r0 = (dma_rank * kInst + q) * C::ROWS_PER_INST;
-        const int r = r0 + lane / C::CH;
-        const int c = (lane % C::CH) ^ swz<D>(r);
-        int tok = tb + r;
-        tok = tok < i_te ? tok : i_te - 1;
-        size_t row;
-        if (paged) {
-          const int blk = sBlk[i_blkoff + tok / bs - i_blk0];
-          row = (static_cast<size_t>(blk) * bs + tok % bs) * p.Hkv + i_hkv;
-        } else {
-          row = (static_cast<size_t>(i_b) * p.T_cap + tok) * p.Hkv + i_hkv;
-        }
-        const size_t off = row * C::ROW + c * 16;
         const uint32_t lk = __builtin_amdgcn_readfirstlane(sbase + r0 * C::ROW);
-        dma16(Kg + off, lk);
-        dma16(Vg + off, lk + C::HALF);
+        dma16(Kg + off[q], lk);
+        dma16(Vg + off[q], lk + C::HALF);
       }
     };
 
